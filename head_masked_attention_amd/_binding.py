@@ -1,0 +1,282 @@
+"""ctypes binding of libbsattn (argument marshalling only).
+
+Every function has the name of the C entry point it calls (``select`` calls
+``bsattn_select`` and so on).  PyTorch supplies device memory and the stream;
+all arithmetic runs in the library's HIP kernels.  There is no fallback: if
+libbsattn.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+
+# haagenti_sparse lib.rs: fraction of heads skipped, and the floor on active heads.
+DEFAULT_SPARSITY = 0.5
+MIN_ACTIVE_HEADS = 4
+
+BF16, F32 = 0, 1
+SEG_KINDS = {"text": 0, "conditioning": 1, "audio": 2, "other": 3,
+             "image": 4, "video": 5, "padding": 6}
+MAX_SEGMENTS = 32
+STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_DTYPE", 3: "ERR_SHAPE", 4: "ERR_STRIDE",
+                5: "ERR_LAYOUT", 6: "ERR_BUDGET", 7: "ERR_WORKSPACE", 8: "ERR_HIP",
+                9: "ERR_UNSUPPORTED"}
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({message})")
+        self.status = status
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class _Segment(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("length", ctypes.c_int64)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("segments", ctypes.POINTER(_Segment)), ("window_tokens", ctypes.c_int32)]
+
+
+class _BlockMask(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("nqb", ctypes.c_int32),
+                ("nkb", ctypes.c_int32), ("mask", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("index", ctypes.c_void_p), ("is_dense", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
+           "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
+           "bsattn_head_mask", "bsattn_mask_density"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libbsattn.so (raises if it is missing: no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with head_masked_attention_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.bsattn_status_string.argtypes = [ctypes.c_int]
+    lib.bsattn_status_string.restype = ctypes.c_char_p
+    lib.bsattn_layout_classes.argtypes = [ctypes.POINTER(_Layout), i64, P, ctypes.POINTER(i32)]
+    lib.bsattn_budget_k.argtypes = [i32, dbl, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.bsattn_select_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
+    lib.bsattn_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsattn_select.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                  ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P,
+                                  ctypes.c_size_t, P]
+    lib.bsattn_radial.argtypes = [ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
+    lib.bsattn_forward.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                   ctypes.POINTER(_Tensor), ctypes.POINTER(_BlockMask), P,
+                                   ctypes.c_float, ctypes.POINTER(_Tensor), P]
+    lib.bsattn_head_mask.argtypes = [P, i32, dbl, i32, P]
+    lib.bsattn_mask_density.argtypes = [ctypes.POINTER(_BlockMask), P, ctypes.POINTER(dbl)]
+    for name in EXPORTS[1:]:
+        if name != "bsattn_select_workspace_bytes":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().bsattn_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise BsattnError(status, where, status_string(status))
+
+
+@dataclass
+class Layout:
+    """Token layout of a packed sequence: ordered (kind, length) segments."""
+    block: int = 64
+    segments: list = field(default_factory=list)
+    window_tokens: int = 0
+
+    def _c(self):
+        n = len(self.segments)
+        arr = (_Segment * max(n, 1))()
+        for i, (kind, length) in enumerate(self.segments):
+            arr[i].kind = SEG_KINDS[kind] if isinstance(kind, str) else int(kind)
+            arr[i].length = int(length)
+        lay = _Layout(self.block, n, ctypes.cast(arr, ctypes.POINTER(_Segment)), self.window_tokens)
+        return lay, arr   # keep arr alive with lay
+
+
+@dataclass
+class BlockMask:
+    """Block mask in CSR-like form; torch tensors on the device."""
+    mask: object      # uint8 [B,H,nqb,nkb]
+    count: object     # int32 [B,H,nqb]
+    index: object     # int32 [B,H,nqb,nkb], first count entries valid
+    is_dense: bool = False
+    k: int = 0
+
+    def _c(self):
+        B, H, nqb, nkb = self.mask.shape
+        return _BlockMask(B, H, nqb, nkb, self.mask.data_ptr(), self.count.data_ptr(),
+                          self.index.data_ptr(), int(self.is_dense), int(self.k))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise BsattnError(2, "tensor", f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t) -> _Tensor:
+    if t.dim() != 4:
+        raise BsattnError(3, "tensor", "expected a [B,H,N,D] tensor")
+    B, H, N, D = t.shape
+    sb, sh, sn, sd = t.stride()
+    if sd != 1 and D > 1:
+        raise BsattnError(4, "tensor", "the D axis must be contiguous")
+    return _Tensor(t.data_ptr(), _dtype_code(t), B, H, N, D, sb, sh, sn)
+
+
+def _stream(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def empty_block_mask(B: int, H: int, nb: int, device) -> BlockMask:
+    import torch
+    return BlockMask(torch.empty((B, H, nb, nb), dtype=torch.uint8, device=device),
+                     torch.empty((B, H, nb), dtype=torch.int32, device=device),
+                     torch.empty((B, H, nb, nb), dtype=torch.int32, device=device))
+
+
+def select_workspace_bytes(B, H, Hkv, N, block, D) -> int:
+    return int(load_library().bsattn_select_workspace_bytes(B, H, Hkv, N, block, D))
+
+
+def select(q, k, layout: Layout, budget: float, *, out: BlockMask | None = None,
+           workspace=None, stream=None) -> BlockMask:
+    """bsattn_select: content-aware block selection (no host sync)."""
+    import torch
+    lib = load_library()
+    B, H, N, D = q.shape
+    nb = N // layout.block
+    if out is None:
+        out = empty_block_mask(B, H, nb, q.device)
+    need = select_workspace_bytes(B, H, k.shape[1], N, layout.block, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    tq, tk = _tensor(q), _tensor(k)
+    lay, _keep = layout._c()
+    bm = out._c()
+    st = lib.bsattn_select(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(lay), float(budget),
+                           ctypes.byref(bm), workspace.data_ptr(), workspace.numel(),
+                           _stream(q.device, stream))
+    _check(st, "bsattn_select")
+    out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
+    return out
+
+
+def radial(layout: Layout, N: int, density: float, *, B: int = 1, H: int = 1, device=None,
+           out: BlockMask | None = None, stream=None) -> BlockMask:
+    """bsattn_radial: layout-only band control at the selector's density."""
+    import torch
+    lib = load_library()
+    nb = N // layout.block
+    if out is None:
+        out = empty_block_mask(B, H, nb, device if device is not None else torch.device("cuda"))
+    lay, _keep = layout._c()
+    bm = out._c()
+    st = lib.bsattn_radial(ctypes.byref(lay), float(density), ctypes.byref(bm),
+                           _stream(out.mask.device, stream))
+    _check(st, "bsattn_radial")
+    out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
+    return out
+
+
+def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale: float = 0.0,
+            *, out=None, stream=None):
+    """bsattn_forward: attention over the kept blocks; masked heads give zeros."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    bm = None if block_mask is None else block_mask._c()
+    hm = None
+    if head_mask is not None:
+        if head_mask.dtype != torch.uint8 or not head_mask.is_cuda:
+            raise BsattnError(2, "bsattn_forward", "head_mask must be a uint8 device tensor")
+        if head_mask.numel() != q.shape[1] or not head_mask.is_contiguous():
+            raise BsattnError(3, "bsattn_forward", "head_mask must hold one byte per query head")
+        hm = head_mask.data_ptr()
+    st = lib.bsattn_forward(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                            None if bm is None else ctypes.byref(bm), hm, float(scale),
+                            ctypes.byref(to), _stream(q.device, stream))
+    _check(st, "bsattn_forward")
+    return out
+
+
+def head_mask(importance, sparsity: float = DEFAULT_SPARSITY,
+              min_active: int = MIN_ACTIVE_HEADS) -> np.ndarray:
+    """bsattn_head_mask (host): keep the most important heads of one layer."""
+    imp = np.ascontiguousarray(importance, dtype=np.float64)
+    out = np.zeros(imp.shape[0], dtype=np.uint8)
+    st = load_library().bsattn_head_mask(imp.ctypes.data_as(ctypes.c_void_p), imp.shape[0],
+                                         float(sparsity), int(min_active),
+                                         out.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "bsattn_head_mask")
+    return out
+
+
+def mask_density(block_mask: BlockMask, stream=None) -> float:
+    """bsattn_mask_density: kept fraction of tiles (synchronises; off the hot path)."""
+    bm = block_mask._c()
+    d = ctypes.c_double()
+    st = load_library().bsattn_mask_density(ctypes.byref(bm),
+                                            _stream(block_mask.count.device, stream),
+                                            ctypes.byref(d))
+    _check(st, "bsattn_mask_density")
+    return float(d.value)
+
+
+def layout_classes(layout: Layout, N: int):
+    """bsattn_layout_classes (host): per-block classes and the candidate count."""
+    lay, _keep = layout._c()
+    nb = N // layout.block
+    cls = np.zeros(max(nb, 1), dtype=np.uint8)
+    n = ctypes.c_int32()
+    st = load_library().bsattn_layout_classes(ctypes.byref(lay), N,
+                                              cls.ctypes.data_as(ctypes.c_void_p),
+                                              ctypes.byref(n))
+    _check(st, "bsattn_layout_classes")
+    return cls[:nb], int(n.value)
+
+
+def budget_k(n_cand: int, budget: float):
+    """bsattn_budget_k (host): (k, is_dense)."""
+    k = ctypes.c_int32()
+    d = ctypes.c_int32()
+    st = load_library().bsattn_budget_k(n_cand, float(budget), ctypes.byref(k), ctypes.byref(d))
+    _check(st, "bsattn_budget_k")
+    return int(k.value), bool(d.value)

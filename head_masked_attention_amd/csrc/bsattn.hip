@@ -1,0 +1,345 @@
+// C-ABI layer of libbsattn: validation, host geometry and launches.
+//
+// Everything that depends only on the layout (block classes, candidate
+// count, k, is_dense, window width) is host arithmetic, so no call ever reads
+// a device value back (SD.Next commit view, modules/attention/sparse,
+// synchronisation paragraph).  Validation returns before any HIP call.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/bsattn.h"
+#include "common.h"
+#include "internal.h"
+
+using namespace bsattn;
+
+namespace {
+
+size_t elem_size(int32_t dtype) { return dtype == BSATTN_F32 ? 4 : 2; }
+
+bool dtype_ok(int32_t dtype) { return dtype == BSATTN_BF16 || dtype == BSATTN_F32; }
+
+// A [B][H][N][D] view: D contiguous, supported D, 16-byte aligned rows.
+bsattn_status check_tensor(const bsattn_tensor* t) {
+    if (t == nullptr || t->data == nullptr) return BSATTN_ERR_NULL;
+    if (!dtype_ok(t->dtype)) return BSATTN_ERR_DTYPE;
+    if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->D <= 0) return BSATTN_ERR_SHAPE;
+    if (t->D != 32 && t->D != 64 && t->D != 128) return BSATTN_ERR_SHAPE;
+    if (t->B > INT32_MAX || t->H > INT32_MAX || t->N > INT32_MAX) return BSATTN_ERR_SHAPE;
+    if (t->stride_b <= 0 || t->stride_h <= 0 || t->stride_n < t->D) return BSATTN_ERR_STRIDE;
+    const size_t es = elem_size(t->dtype);
+    if (((uintptr_t)t->data) % 16 != 0) return BSATTN_ERR_STRIDE;
+    if ((t->stride_b * es) % 16 || (t->stride_h * es) % 16 || (t->stride_n * es) % 16)
+        return BSATTN_ERR_STRIDE;
+    return BSATTN_OK;
+}
+
+TView view_of(const bsattn_tensor* t) {
+    return TView{t->data, t->stride_b, t->stride_h, t->stride_n};
+}
+
+bool budget_ok(double x) { return std::isfinite(x) && x > 0.0; }
+
+// Block classes from ordered segments: a block is DROPPED when every segment
+// it overlaps is padding, SPARSE when it lies inside one image/video segment,
+// PINNED otherwise.  Returns false on a malformed layout.
+bool compute_classes(const bsattn_layout* lay, int64_t N, std::vector<int32_t>& cls) {
+    const int64_t block = lay->block;
+    const int64_t nb = N / block;
+    cls.assign((size_t)nb, CLS_SPARSE);
+    if (lay->n_segments == 0) return true;
+    int64_t total = 0;
+    for (int s = 0; s < lay->n_segments; ++s) {
+        const bsattn_segment& sg = lay->segments[s];
+        if (sg.length <= 0 || sg.kind < BSATTN_SEG_TEXT || sg.kind > BSATTN_SEG_PADDING) return false;
+        total += sg.length;
+    }
+    if (total != N) return false;
+    int s = 0;
+    int64_t seg_start = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = b * block, hi = lo + block;   // [lo, hi)
+        while (seg_start + lay->segments[s].length <= lo) { seg_start += lay->segments[s].length; ++s; }
+        bool all_pad = true, single = true, sparsifiable = true;
+        int64_t st = seg_start;
+        for (int u = s; u < lay->n_segments && st < hi; st += lay->segments[u].length, ++u) {
+            const int32_t kd = lay->segments[u].kind;
+            if (kd != BSATTN_SEG_PADDING) all_pad = false;
+            if (kd != BSATTN_SEG_IMAGE && kd != BSATTN_SEG_VIDEO) sparsifiable = false;
+            if (u != s) single = false;
+        }
+        cls[(size_t)b] = all_pad ? CLS_DROPPED : (single && sparsifiable) ? CLS_SPARSE : CLS_PINNED;
+    }
+    return true;
+}
+
+void budget_rule(int32_t n_cand, double budget, int32_t* k, int32_t* is_dense) {
+    if (n_cand <= 0) { *k = 0; *is_dense = 1; return; }
+    const double x = std::floor(budget * (double)n_cand + 1e-9);
+    int32_t kk = x >= (double)n_cand ? n_cand : (int32_t)x;
+    if (kk < 1) kk = 1;
+    *k = kk;
+    *is_dense = kk >= n_cand ? 1 : 0;
+}
+
+// Window half-width in blocks: the largest d with a token pair of blocks d
+// apart within W/2, i.e. 2 * ((d - 1) * block + 1) <= W.
+int32_t window_blocks(int32_t W, int32_t block) {
+    if (W <= 0) return -1;
+    if (W < 2) return 0;
+    return (W - 2) / (2 * block) + 1;
+}
+
+bsattn_status check_layout(const bsattn_layout* lay) {
+    if (lay == nullptr) return BSATTN_ERR_NULL;
+    if (lay->block != 32 && lay->block != 64) return BSATTN_ERR_SHAPE;
+    if (lay->n_segments < 0 || lay->n_segments > BSATTN_MAX_SEGMENTS) return BSATTN_ERR_LAYOUT;
+    if (lay->n_segments > 0 && lay->segments == nullptr) return BSATTN_ERR_NULL;
+    if (lay->window_tokens < 0) return BSATTN_ERR_LAYOUT;
+    return BSATTN_OK;
+}
+
+bsattn_status make_geometry(const bsattn_layout* lay, int64_t N, double budget, Geometry& g) {
+    std::vector<int32_t> cls;
+    if (!compute_classes(lay, N, cls)) return BSATTN_ERR_LAYOUT;
+    std::memset(&g, 0, sizeof g);
+    g.nb = (int32_t)(N / lay->block);
+    g.block = lay->block;
+    int32_t n_sparse = 0, n_other = 0, runs = 0;
+    for (int32_t b = 0; b < g.nb;) {
+        int32_t e = b;
+        while (e < g.nb && cls[(size_t)e] == cls[(size_t)b]) ++e;
+        if (runs == kMaxRuns) return BSATTN_ERR_LAYOUT;
+        g.run_first[runs] = b;
+        g.run_len[runs] = e - b;
+        g.run_cls[runs] = cls[(size_t)b];
+        if (cls[(size_t)b] == CLS_SPARSE) { g.run_off[runs] = n_sparse; n_sparse += e - b; }
+        else { g.run_off[runs] = n_other; n_other += e - b; }
+        ++runs;
+        b = e;
+    }
+    g.n_runs = runs;
+    g.n_cand = n_sparse;
+    g.n_other = n_other;
+    budget_rule(n_sparse, budget, &g.k, &g.is_dense);
+    g.w = window_blocks(lay->window_tokens, lay->block);
+    return BSATTN_OK;
+}
+
+bsattn_status check_mask_out(const bsattn_block_mask* m) {
+    if (m == nullptr || m->mask == nullptr || m->count == nullptr || m->index == nullptr)
+        return BSATTN_ERR_NULL;
+    if (m->B <= 0 || m->H <= 0 || m->nqb <= 0 || m->nqb != m->nkb) return BSATTN_ERR_SHAPE;
+    return BSATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsattn_status_string(bsattn_status st) {
+    switch (st) {
+        case BSATTN_OK: return "ok";
+        case BSATTN_ERR_NULL: return "required pointer is NULL";
+        case BSATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
+        case BSATTN_ERR_SHAPE: return "inconsistent or unsupported shape";
+        case BSATTN_ERR_STRIDE: return "bad stride or misaligned pointer";
+        case BSATTN_ERR_LAYOUT: return "malformed token layout";
+        case BSATTN_ERR_BUDGET: return "budget/density or head-mask arguments out of range";
+        case BSATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case BSATTN_ERR_HIP: return "HIP runtime error";
+        case BSATTN_ERR_UNSUPPORTED: return "no kernel for this configuration";
+    }
+    return "unknown status";
+}
+
+bsattn_status bsattn_layout_classes(const bsattn_layout* layout, int64_t N, uint8_t* classes,
+                                    int32_t* n_cand) {
+    bsattn_status st = check_layout(layout);
+    if (st != BSATTN_OK) return st;
+    if (classes == nullptr || n_cand == nullptr) return BSATTN_ERR_NULL;
+    if (N <= 0 || N % layout->block != 0 || N / layout->block > INT32_MAX) return BSATTN_ERR_SHAPE;
+    std::vector<int32_t> cls;
+    if (!compute_classes(layout, N, cls)) return BSATTN_ERR_LAYOUT;
+    int32_t nc = 0;
+    for (size_t b = 0; b < cls.size(); ++b) {
+        classes[b] = (uint8_t)cls[b];
+        nc += cls[b] == CLS_SPARSE;
+    }
+    *n_cand = nc;
+    return BSATTN_OK;
+}
+
+bsattn_status bsattn_budget_k(int32_t n_cand, double budget, int32_t* k, int32_t* is_dense) {
+    if (k == nullptr || is_dense == nullptr) return BSATTN_ERR_NULL;
+    if (n_cand < 0) return BSATTN_ERR_SHAPE;
+    if (!budget_ok(budget)) return BSATTN_ERR_BUDGET;
+    budget_rule(n_cand, budget, k, is_dense);
+    return BSATTN_OK;
+}
+
+size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int32_t block,
+                                     int64_t D) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || (block != 32 && block != 64)) return 0;
+    const size_t nb = (size_t)(N / block);
+    return align256((size_t)B * H * nb * D * 4) + align256((size_t)B * Hkv * nb * D * 4);
+}
+
+bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
+                            const bsattn_layout* layout, double budget, bsattn_block_mask* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    bsattn_status st;
+    if ((st = check_tensor(q)) != BSATTN_OK) return st;
+    if ((st = check_tensor(k)) != BSATTN_OK) return st;
+    if ((st = check_layout(layout)) != BSATTN_OK) return st;
+    if (out == nullptr) return BSATTN_ERR_NULL;
+    if ((st = check_mask_out(out)) != BSATTN_OK) return st;
+    if (q->dtype != k->dtype) return BSATTN_ERR_DTYPE;
+    if (q->B != k->B || q->N != k->N || q->D != k->D) return BSATTN_ERR_SHAPE;
+    if (q->H % k->H != 0) return BSATTN_ERR_SHAPE;
+    if (q->N % layout->block != 0) return BSATTN_ERR_SHAPE;
+    const int64_t nb = q->N / layout->block;
+    if (out->B != q->B || out->H != q->H || out->nqb != nb) return BSATTN_ERR_SHAPE;
+    if (!budget_ok(budget)) return BSATTN_ERR_BUDGET;
+    Geometry g;
+    if ((st = make_geometry(layout, q->N, budget, g)) != BSATTN_OK) return st;
+    if (!g.is_dense && g.n_cand > kMaxCand) return BSATTN_ERR_UNSUPPORTED;
+    const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, layout->block, q->D);
+    if (!g.is_dense) {
+        if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;
+        if (workspace_bytes < need || ((uintptr_t)workspace) % 256 != 0) return BSATTN_ERR_WORKSPACE;
+    }
+
+    const hipStream_t s = (hipStream_t)stream;
+    const MaskOut mo{out->mask, out->count, out->index};
+    out->k = g.k;
+    out->is_dense = g.is_dense;
+    hipError_t e;
+    if (g.is_dense) {
+        e = launch_layout_fill(g, (int)(q->B * q->H), mo, s);
+    } else {
+        float* qp = (float*)workspace;
+        float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * nb * q->D * 4));
+        e = launch_pool(q->dtype == BSATTN_F32, (int)q->D, layout->block, view_of(q), view_of(k),
+                        (int)q->B, (int)q->H, (int)k->H, g, qp, kp, s);
+        if (e == hipSuccess)
+            e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, s);
+    }
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_radial(const bsattn_layout* layout, double density, bsattn_block_mask* out,
+                            void* stream) {
+    bsattn_status st;
+    if ((st = check_layout(layout)) != BSATTN_OK) return st;
+    if (out == nullptr) return BSATTN_ERR_NULL;
+    if ((st = check_mask_out(out)) != BSATTN_OK) return st;
+    if (!budget_ok(density)) return BSATTN_ERR_BUDGET;
+    const int64_t N = (int64_t)out->nqb * layout->block;
+    Geometry g;
+    if ((st = make_geometry(layout, N, density, g)) != BSATTN_OK) return st;
+    out->k = g.k;
+    out->is_dense = g.is_dense;
+    const MaskOut mo{out->mask, out->count, out->index};
+    const hipError_t e = launch_layout_fill(g, out->B * out->H, mo, (hipStream_t)stream);
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
+                             const bsattn_tensor* v, const bsattn_block_mask* mask,
+                             const uint8_t* head_mask, float scale, bsattn_tensor* out,
+                             void* stream) {
+    bsattn_status st;
+    if ((st = check_tensor(q)) != BSATTN_OK) return st;
+    if ((st = check_tensor(k)) != BSATTN_OK) return st;
+    if ((st = check_tensor(v)) != BSATTN_OK) return st;
+    if ((st = check_tensor(out)) != BSATTN_OK) return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype) return BSATTN_ERR_DTYPE;
+    if (k->B != q->B || v->B != q->B || out->B != q->B) return BSATTN_ERR_SHAPE;
+    if (k->N != q->N || v->N != q->N || out->N != q->N) return BSATTN_ERR_SHAPE;
+    if (k->D != q->D || v->D != q->D || out->D != q->D) return BSATTN_ERR_SHAPE;
+    if (v->H != k->H || out->H != q->H || q->H % k->H != 0) return BSATTN_ERR_SHAPE;
+    int64_t block;
+    if (mask == nullptr) {
+        block = 64;
+        if (q->N % block != 0) return BSATTN_ERR_SHAPE;
+    } else {
+        if (mask->count == nullptr || mask->index == nullptr) return BSATTN_ERR_NULL;
+        if (mask->nqb <= 0 || mask->nqb != mask->nkb || q->N % mask->nqb != 0) return BSATTN_ERR_SHAPE;
+        block = q->N / mask->nqb;
+        if (block != 32 && block != 64) return BSATTN_ERR_SHAPE;
+        if (!(mask->B == 1 || mask->B == q->B) || !(mask->H == 1 || mask->H == q->H))
+            return BSATTN_ERR_SHAPE;
+    }
+    if (!(std::isfinite(scale))) return BSATTN_ERR_BUDGET;
+
+    AttnArgs a;
+    a.q = view_of(q);
+    a.k = view_of(k);
+    a.v = view_of(v);
+    a.o = out->data;
+    a.o_sb = out->stride_b;
+    a.o_sh = out->stride_h;
+    a.o_sn = out->stride_n;
+    a.B = (int32_t)q->B;
+    a.H = (int32_t)q->H;
+    a.Hkv = (int32_t)k->H;
+    a.nqb = (int32_t)(q->N / block);
+    a.nkb = a.nqb;
+    a.mB = mask ? mask->B : 1;
+    a.mH = mask ? mask->H : 1;
+    a.count = mask ? mask->count : nullptr;
+    a.index = mask ? mask->index : nullptr;
+    a.head_mask = head_mask;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    a.n_work = (int64_t)a.B * a.H * a.nqb;
+
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (q->dtype == BSATTN_BF16 && block == 64 && (q->D == 64 || q->D == 128))
+        e = launch_attn_mfma(a, (int)q->D, s);
+    else
+        e = launch_attn_vec(a, q->dtype == BSATTN_F32, (int)q->D, (int)block, s);
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_head_mask(const double* importance, int32_t H, double sparsity,
+                               int32_t min_active, uint8_t* out) {
+    if (importance == nullptr || out == nullptr) return BSATTN_ERR_NULL;
+    if (H <= 0) return BSATTN_ERR_SHAPE;
+    if (!(sparsity >= 0.0 && sparsity <= 1.0) || min_active < 0) return BSATTN_ERR_BUDGET;
+    for (int32_t h = 0; h < H; ++h)
+        if (!std::isfinite(importance[h])) return BSATTN_ERR_BUDGET;
+    int32_t n_act = H - (int32_t)std::floor(sparsity * (double)H);
+    if (n_act < min_active) n_act = min_active;
+    if (n_act > H) n_act = H;
+    // a head is kept when fewer than n_act heads rank above it
+    for (int32_t h = 0; h < H; ++h) {
+        int32_t above = 0;
+        for (int32_t o = 0; o < H; ++o)
+            above += importance[o] > importance[h] || (importance[o] == importance[h] && o < h);
+        out[h] = above < n_act ? 1 : 0;
+    }
+    return BSATTN_OK;
+}
+
+bsattn_status bsattn_mask_density(const bsattn_block_mask* m, void* stream, double* density) {
+    if (m == nullptr || m->count == nullptr || density == nullptr) return BSATTN_ERR_NULL;
+    if (m->B <= 0 || m->H <= 0 || m->nqb <= 0 || m->nkb <= 0) return BSATTN_ERR_SHAPE;
+    const size_t rows = (size_t)m->B * m->H * m->nqb;
+    std::vector<int32_t> host(rows);
+    const hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(host.data(), m->count, rows * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return BSATTN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BSATTN_ERR_HIP;
+    double kept = 0.0;
+    for (size_t r = 0; r < rows; ++r) kept += host[r];
+    *density = kept / ((double)rows * m->nkb);
+    return BSATTN_OK;
+}
+
+}  // extern "C"

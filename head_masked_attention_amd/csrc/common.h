@@ -1,0 +1,98 @@
+// Shared device/host definitions of libbsattn (gfx950).
+//
+// The layout of a packed sequence reaches the kernels as a run-length
+// encoding of the per-block classes, passed by value as a kernel argument
+// (no host-to-device copy and no device state): the SD.Next synchronisation
+// paragraph moves everything that depends only on geometry and layout to the
+// host, so a call never reads a device value back.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+enum BlockClass : int32_t { CLS_SPARSE = 0, CLS_PINNED = 1, CLS_DROPPED = 2 };
+
+constexpr int kMaxRuns = 72;      // class runs; <= 2 * BSATTN_MAX_SEGMENTS + 1 in practice
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kMaxCand = 2048;    // sparsifiable blocks handled by the selector
+
+// Per-layout geometry, host-computed once per call and passed by value.
+struct Geometry {
+    int32_t nb;          // blocks in the sequence (N / block)
+    int32_t block;       // tokens per block
+    int32_t n_cand;      // SPARSE blocks (selector candidates)
+    int32_t n_other;     // PINNED + DROPPED blocks
+    int32_t k;           // candidates kept per SPARSE row
+    int32_t is_dense;    // k >= n_cand
+    int32_t w;           // window half-width in blocks, -1 = no window
+    int32_t n_runs;
+    int32_t run_first[kMaxRuns];   // first block of the run
+    int32_t run_len[kMaxRuns];     // blocks in the run
+    int32_t run_cls[kMaxRuns];     // BlockClass of every block in the run
+    int32_t run_off[kMaxRuns];     // position of run_first among blocks of the
+                                   // same group (SPARSE, or PINNED+DROPPED)
+};
+
+// Strided view of a [B][H][N][D] tensor; D contiguous.  Strides in elements.
+struct TView {
+    const void* p;
+    int64_t sb, sh, sn;
+};
+
+struct MaskOut {
+    uint8_t* mask;       // [B][H][nqb][nkb]
+    int32_t* count;      // [B][H][nqb]
+    int32_t* index;      // [B][H][nqb][nkb]
+};
+
+// ---- run lookups (runs are few; a linear scan is cheapest) ----------------
+
+__device__ __forceinline__ int32_t block_class(const Geometry& g, int32_t j) {
+    for (int r = 0; r < g.n_runs; ++r)
+        if (j < g.run_first[r] + g.run_len[r]) return g.run_cls[r];
+    return CLS_DROPPED;
+}
+
+// Block index of the pos-th SPARSE block.
+__device__ __forceinline__ int32_t cand_block(const Geometry& g, int32_t pos) {
+    for (int r = 0; r < g.n_runs; ++r)
+        if (g.run_cls[r] == CLS_SPARSE && pos < g.run_off[r] + g.run_len[r])
+            return g.run_first[r] + (pos - g.run_off[r]);
+    return -1;
+}
+
+// Block index of the pos-th non-SPARSE block.
+__device__ __forceinline__ int32_t other_block(const Geometry& g, int32_t pos) {
+    for (int r = 0; r < g.n_runs; ++r)
+        if (g.run_cls[r] != CLS_SPARSE && pos < g.run_off[r] + g.run_len[r])
+            return g.run_first[r] + (pos - g.run_off[r]);
+    return -1;
+}
+
+// Column code used by the compaction passes: candidate position (>= 0) for a
+// SPARSE block, -1 for PINNED, -2 for DROPPED.
+__device__ __forceinline__ int32_t column_code(const Geometry& g, int32_t j) {
+    for (int r = 0; r < g.n_runs; ++r)
+        if (j < g.run_first[r] + g.run_len[r]) {
+            if (g.run_cls[r] == CLS_SPARSE) return g.run_off[r] + (j - g.run_first[r]);
+            return g.run_cls[r] == CLS_PINNED ? -1 : -2;
+        }
+    return -2;
+}
+
+// XCD-aware workgroup order: hardware workgroup w runs on XCD w % 8, so the
+// logical id groups consecutive logical work (the query blocks of one head)
+// on one XCD and its L2.  `padded` is the launched grid, a multiple of 8;
+// logical ids >= the real count exit.
+__device__ __forceinline__ int64_t xcd_logical_id(int64_t w, int64_t padded) {
+    const int64_t per = padded / kNumXcd;
+    return (w % kNumXcd) * per + (w / kNumXcd);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+}  // namespace bsattn

@@ -1,0 +1,33 @@
+// Kernel launchers shared between the C-ABI layer and the kernel sources.
+#pragma once
+
+#include "common.h"
+
+namespace bsattn {
+
+// Arguments of the attention kernels (by value).
+struct AttnArgs {
+    TView q, k, v;
+    void* o;
+    int64_t o_sb, o_sh, o_sn;
+    int32_t B, H, Hkv, nqb, nkb;
+    int32_t mB, mH;              // mask batch/head extents (1 = shared)
+    const int32_t* count;        // NULL = dense (every block kept)
+    const int32_t* index;
+    const uint8_t* head_mask;    // NULL = every head active
+    float scale;                 // softmax scale (> 0)
+    int64_t n_work;              // B * H * nqb workgroups of real work
+};
+
+hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
+                       int Hkv, const Geometry& g, float* qp, float* kp, hipStream_t s);
+hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
+                             const Geometry& g, MaskOut out, hipStream_t s);
+hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
+
+// bf16, block 64, D in {64, 128}: MFMA path.
+hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s);
+// any supported dtype / block / D: fp32 vector path.
+hipError_t launch_attn_vec(const AttnArgs& a, int dtype_is_f32, int D, int block, hipStream_t s);
+
+}  // namespace bsattn

@@ -1,0 +1,373 @@
+// Selector kernels of libbsattn (gfx950).
+//
+//  pool_kernel        block sums of Q and K over the SPARSE blocks (HBM bound;
+//                     16-byte coalesced loads, fp32 accumulation).
+//  score_rank_kernel  per (b, h, tile of candidate rows): fp32 MFMA scores of
+//                     every candidate pair, a wavefront bitonic sort of each
+//                     row with ties to the lower block index, then pins,
+//                     drops, the sliding window and CSR compaction.  PINNED and
+//                     DROPPED rows are written by the same launch.
+//  layout_kernel      the radial band and the layout-only (dense) mask.
+//
+// SD.Next commit view, modules/attention/sparse: the selector paragraph
+// (tile mean-pooling, unscaled pair scores, a per-row budget over the
+// sparsifiable candidates, diagonal kept, full budget reports dense), the
+// layout paragraph (pins and drops), the radial-control paragraph (band at the
+// selector's density honouring the pins) and the synchronisation paragraph
+// (ranking replaces a host-sized top-k; no host sync anywhere here).
+#include "common.h"
+#include "internal.h"
+
+namespace bsattn {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// K1: block sums.  One wavefront per (tensor, b, head, candidate block).
+// Ranking by <sum Q_i, sum K_j> equals ranking by the mean-pooled score: the
+// factor 1/block^2 is a positive constant.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BLOCK>
+__global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int H, int Hkv,
+                                                   Geometry g, float* __restrict__ qp,
+                                                   float* __restrict__ kp) {
+    constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;               // chunks per token row
+    constexpr int RPI = 64 / CPR;              // token rows per wave instruction
+    constexpr int NL = BLOCK / RPI;            // loads per lane
+    static_assert(CPR <= 64 && 64 % CPR == 0 && BLOCK % RPI == 0, "pool geometry");
+
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nq = (int64_t)B * H * g.n_cand;
+    const int64_t nk = (int64_t)B * Hkv * g.n_cand;
+    if (item >= nq + nk) return;
+
+    const TView* src;
+    int64_t rem, heads;
+    float* dst;
+    if (item < nq) { src = &q; rem = item; heads = H; dst = qp + item * D; }
+    else { src = &k; rem = item - nq; heads = Hkv; dst = kp + rem * D; }
+    const int64_t p = rem % g.n_cand;
+    const int64_t hh = (rem / g.n_cand) % heads;
+    const int64_t b = rem / (g.n_cand * heads);
+    const int64_t blk = cand_block(g, (int32_t)p);
+
+    const T* base = (const T*)src->p + b * src->sb + hh * src->sh +
+                    (blk * BLOCK + lane / CPR) * src->sn + (lane % CPR) * EPC;
+    uint4 raw[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+        raw[l] = *(const uint4*)(base + (int64_t)l * RPI * src->sn);
+
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += __uint_as_float(w[e] << 16);
+                acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+        }
+    }
+    // lanes holding the same chunk of different rows: lane % CPR equal
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+
+    if (lane < CPR) {
+        float* o = dst + lane * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) *(f4v*)(o + e) = f4v{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    }
+}
+
+// Order-preserving map of a float to uint32 (-0 taken as +0).
+__device__ __forceinline__ uint32_t orderable(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;                       // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = __shfl_xor((uint32_t)v, m);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of 64*E keys spread over one wavefront; element
+// e = lane * E + r lives in key[r].
+template <int E>
+__device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[E], int lane) {
+    constexpr int NTOT = 64 * E;
+#pragma unroll
+    for (int size = 2; size <= NTOT; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride < E) {
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    if (r & stride) continue;
+                    const int e = lane * E + r;
+                    const bool desc = (e & size) == 0;
+                    const uint64_t a = key[r], b = key[r | stride];
+                    const bool swap = desc ? (a < b) : (a > b);
+                    key[r] = swap ? b : a;
+                    key[r | stride] = swap ? a : b;
+                }
+            } else {
+                const int lm = stride / E;
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int e = lane * E + r;
+                    const uint64_t other = shfl_xor_u64(key[r], lm);
+                    const bool lower = (e & stride) == 0;
+                    const bool desc = (e & size) == 0;
+                    const uint64_t mx = key[r] > other ? key[r] : other;
+                    const uint64_t mn = key[r] > other ? other : key[r];
+                    key[r] = (lower == desc) ? mx : mn;
+                }
+            }
+        }
+    }
+}
+
+// Writes one mask row (all nkb columns), its ascending index list and count,
+// with one wavefront.  keep(j, code) decides SPARSE columns; PINNED columns
+// are kept and DROPPED ones are not, unless `row_dropped` (then nothing).
+template <typename KeepFn>
+__device__ __forceinline__ void compact_row(const Geometry& g, int lane, bool row_dropped,
+                                            bool row_pinned, uint8_t* mrow, int32_t* irow,
+                                            int32_t* cnt_out, KeepFn keep) {
+    int32_t cnt = 0;
+    for (int32_t j0 = 0; j0 < g.nb; j0 += 64) {
+        const int32_t j = j0 + lane;
+        bool v = false;
+        if (j < g.nb && !row_dropped) {
+            const int32_t code = column_code(g, j);
+            if (code == -2) v = false;
+            else if (code == -1 || row_pinned) v = true;
+            else v = keep(j, code);
+        }
+        const uint64_t bal = __ballot(v);
+        const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (v) irow[cnt + before] = j;
+        if (j < g.nb) mrow[j] = v ? 1 : 0;
+        cnt += __popcll(bal);
+    }
+    if (lane == 0) *cnt_out = cnt;
+}
+
+// ---------------------------------------------------------------------------
+// K2: scores, rank and compaction for one (b, h) and RT candidate rows.
+// The workgroup also writes its share of the PINNED/DROPPED rows.
+// ---------------------------------------------------------------------------
+template <int D, int E>
+__global__ __launch_bounds__(256) void score_rank_kernel(const float* __restrict__ qp,
+                                                         const float* __restrict__ kp, int B,
+                                                         int H, int Hkv, Geometry g, MaskOut out,
+                                                         int n_tiles) {
+    constexpr int NPAD = 64 * E;
+    constexpr int RT = (E <= 8) ? 32 : 16;     // candidate rows per workgroup
+    constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
+    constexpr int KQ = D / 4;                  // MFMA k-steps; lane group gq owns d in [gq*KQ, gq*KQ+KQ)
+    __shared__ float s_score[RT * SSTR];
+    __shared__ uint8_t s_keep[4][NPAD];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x % n_tiles;
+    const int64_t bh = blockIdx.x / n_tiles;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t g_kv = h / (H / Hkv);
+    const int p0 = tile * RT;
+    const int rows = min(RT, g.n_cand - p0);
+
+    const float* qbase = qp + (bh * g.n_cand) * (int64_t)D;
+    const float* kbase = kp + ((b * Hkv + g_kv) * g.n_cand) * (int64_t)D;
+
+    // ---- scores S[p0 + r][c] = <Qsum_(p0+r), Ksum_c> with fp32 MFMA 16x16x4
+    const int li = lane & 15, gq = lane >> 4;
+    f4v a[RT / 16][KQ / 4];
+#pragma unroll
+    for (int rt = 0; rt < RT / 16; ++rt) {
+        const int pr = min(p0 + rt * 16 + li, g.n_cand - 1);
+        const f4v* src = (const f4v*)(qbase + (int64_t)pr * D + gq * KQ);
+#pragma unroll
+        for (int c = 0; c < KQ / 4; ++c) a[rt][c] = src[c];
+    }
+    const int n_ct = (g.n_cand + 15) / 16;
+    for (int ct = wave; ct < n_ct; ct += 4) {
+        const int jc = min(ct * 16 + li, g.n_cand - 1);
+        const f4v* src = (const f4v*)(kbase + (int64_t)jc * D + gq * KQ);
+        f4v bv[KQ / 4];
+#pragma unroll
+        for (int c = 0; c < KQ / 4; ++c) bv[c] = src[c];
+#pragma unroll
+        for (int rt = 0; rt < RT / 16; ++rt) {
+            f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KQ / 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt][c][e], bv[c][e], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                s_score[(rt * 16 + 4 * gq + r) * SSTR + ct * 16 + li] = acc[r];
+        }
+    }
+    __syncthreads();
+
+    const int64_t slice = b * H + h;
+    const int64_t nb = g.nb;
+    // ---- per row: bitonic rank, keep the first k, compact
+    for (int r0 = 0; r0 < RT; r0 += 4) {
+        const int rl = r0 + wave;
+        if (rl < rows) {
+            const int p = p0 + rl;
+            uint64_t key[E];
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const int pos = lane * E + r;
+                const uint32_t low = 0xffffffffu - (uint32_t)pos;
+                if (pos >= g.n_cand) key[r] = 0ull;
+                else if (pos == p) key[r] = (0xffffffffull << 32) | low;
+                else key[r] = ((uint64_t)orderable(s_score[rl * SSTR + pos]) << 32) | low;
+            }
+            wave_bitonic_desc<E>(key, lane);
+#pragma unroll
+            for (int r = 0; r < E; ++r) s_keep[wave][lane * E + r] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (lane * E + r < g.k) s_keep[wave][0xffffffffu - (uint32_t)key[r]] = 1;
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+
+            const int32_t i = cand_block(g, p);
+            const uint8_t* kp_row = s_keep[wave];
+            const int32_t w = g.w;
+            compact_row(g, lane, false, false, out.mask + (slice * nb + i) * nb,
+                        out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
+                        [&](int32_t j, int32_t code) {
+                            return kp_row[code] != 0 || (w >= 0 && abs(j - i) <= w);
+                        });
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+
+    // ---- this workgroup's share of the PINNED and DROPPED rows
+    for (int t = tile * 4 + wave; t < g.n_other; t += n_tiles * 4) {
+        const int32_t i = other_block(g, t);
+        const int32_t cls = block_class(g, i);
+        compact_row(g, lane, cls == CLS_DROPPED, cls == CLS_PINNED,
+                    out.mask + (slice * nb + i) * nb, out.index + (slice * nb + i) * nb,
+                    out.count + slice * nb + i, [](int32_t, int32_t) { return false; });
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K3: layout-only masks.  Each SPARSE row keeps the k candidates nearest the
+// diagonal by (|i - j|, j) — a contiguous run of candidate positions — plus
+// the window; k = n_cand gives the dense (layout-only) mask.  grid.y = slice.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
+    const int lane = threadIdx.x & 63;
+    const int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= g.nb) return;
+    const int64_t slice = blockIdx.y;
+    const int64_t nb = g.nb;
+    const int32_t code_i = column_code(g, i);
+
+    int32_t lo = 0, kk = g.n_cand;
+    if (code_i >= 0 && !g.is_dense) {
+        kk = g.k;
+        int32_t L = code_i - 1, R = code_i + 1;
+        if (lane == 0) {
+            for (int taken = 1; taken < kk; ++taken) {
+                bool take_left;
+                if (L < 0) take_left = false;
+                else if (R >= g.n_cand) take_left = true;
+                else take_left = (i - cand_block(g, L)) <= (cand_block(g, R) - i);
+                if (take_left) --L; else ++R;
+            }
+        }
+        lo = __shfl(L + 1, 0);
+    }
+    const int32_t w = g.w;
+    compact_row(g, lane, code_i == -2, code_i == -1, out.mask + (slice * nb + i) * nb,
+                out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
+                [&](int32_t j, int32_t code) {
+                    return (code >= lo && code < lo + kk) || (w >= 0 && abs(j - i) <= w);
+                });
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
+                                const Geometry& g, float* qp, float* kp, hipStream_t s) {
+    const int64_t items = (int64_t)B * (H + Hkv) * g.n_cand;
+    const dim3 grid((unsigned)((items + 3) / 4));
+    if (block == 64) hipLaunchKernelGGL((pool_kernel<T, D, 64>), grid, dim3(256), 0, s, q, k, B, H, Hkv, g, qp, kp);
+    else hipLaunchKernelGGL((pool_kernel<T, D, 32>), grid, dim3(256), 0, s, q, k, B, H, Hkv, g, qp, kp);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
+                       int Hkv, const Geometry& g, float* qp, float* kp, hipStream_t s) {
+    if (dtype_is_f32) {
+        if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, s);
+        if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, s);
+        return launch_pool_t<float, 128>(block, q, k, B, H, Hkv, g, qp, kp, s);
+    }
+    if (D == 32) return launch_pool_t<uint16_t, 32>(block, q, k, B, H, Hkv, g, qp, kp, s);
+    if (D == 64) return launch_pool_t<uint16_t, 64>(block, q, k, B, H, Hkv, g, qp, kp, s);
+    return launch_pool_t<uint16_t, 128>(block, q, k, B, H, Hkv, g, qp, kp, s);
+}
+
+template <int D, int E>
+static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H, int Hkv,
+                                 const Geometry& g, MaskOut out, hipStream_t s) {
+    constexpr int RT = (E <= 8) ? 32 : 16;
+    const int n_tiles = (g.n_cand + RT - 1) / RT;
+    const dim3 grid((unsigned)((int64_t)B * H * n_tiles));
+    hipLaunchKernelGGL((score_rank_kernel<D, E>), grid, dim3(256), 0, s, qp, kp, B, H, Hkv, g, out, n_tiles);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_score_d(const float* qp, const float* kp, int B, int H, int Hkv,
+                                 const Geometry& g, MaskOut out, hipStream_t s) {
+    const int n = g.n_cand;
+    if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, s);
+    if (n <= 128) return launch_score_t<D, 2>(qp, kp, B, H, Hkv, g, out, s);
+    if (n <= 256) return launch_score_t<D, 4>(qp, kp, B, H, Hkv, g, out, s);
+    if (n <= 512) return launch_score_t<D, 8>(qp, kp, B, H, Hkv, g, out, s);
+    if (n <= 1024) return launch_score_t<D, 16>(qp, kp, B, H, Hkv, g, out, s);
+    return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, s);
+}
+
+hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
+                             const Geometry& g, MaskOut out, hipStream_t s) {
+    if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, s);
+    if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, s);
+    return launch_score_d<128>(qp, kp, B, H, Hkv, g, out, s);
+}
+
+hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s) {
+    const dim3 grid((unsigned)((g.nb + 3) / 4), (unsigned)slices);
+    hipLaunchKernelGGL(layout_kernel, grid, dim3(256), 0, s, g, out);
+    return hipGetLastError();
+}
+
+}  // namespace bsattn

@@ -1,0 +1,247 @@
+/*
+ * libbsattn — content-aware block-sparse, head-masked self-attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Device buffers are allocated by the
+ * caller; the library allocates no device memory, keeps no device state and
+ * keeps no pointer after a call returns.  Every GPU call only enqueues work on
+ * the caller's HIP stream (passed as `void*`, a hipStream_t; NULL = the null
+ * stream) and never synchronises, except bsattn_mask_density, which is meant
+ * to be called off the hot path.
+ *
+ * Errors: every function returns a bsattn_status.  Validation failures return
+ * before anything is enqueued and leave every output untouched.  A failed
+ * launch returns BSATTN_ERR_HIP.  Device faults surface at the caller's next
+ * synchronisation.  Nothing is printed and nothing exits.
+ *
+ * The library is stateless, so calls are thread-safe.  Calls that share
+ * output buffers on one stream are ordered by the stream; across streams the
+ * caller orders them.
+ *
+ * Sources, pages in the reference bundle:
+ *  - SD.Next commit view, modules/attention/sparse: the selector paragraph,
+ *    the layout paragraph, the radial-control paragraph, the synchronisation
+ *    paragraph (three host syncs per call removed: ranking instead of a
+ *    host-sized top-k, per-layout geometry, lazy density), the live-runs
+ *    paragraph (text padded to 512, sequence to a multiple of 256, padding
+ *    dropped) and the flex-consumer paragraph (only selected tiles computed).
+ *  - haagenti_sparse crate docs and lib.rs: per-layer head masks (AttentionMask,
+ *    MaskBuilder), DEFAULT_SPARSITY = 0.5 (fraction of heads skipped),
+ *    MIN_ACTIVE_HEADS = 4, SparseError/Result as status codes.
+ *  - inferensys glossary "Sparse Attention": sliding-window and block-sparse
+ *    entries; the CSR-like per-row list of kept blocks.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (the crate's SparseError/Result convention as plain ints). */
+typedef enum {
+    BSATTN_OK = 0,
+    BSATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    BSATTN_ERR_DTYPE = 2,       /* unknown dtype, or q/k/v/out dtypes differ           */
+    BSATTN_ERR_SHAPE = 3,       /* sizes inconsistent or outside the supported set     */
+    BSATTN_ERR_STRIDE = 4,      /* negative/overlapping strides or misaligned pointers */
+    BSATTN_ERR_LAYOUT = 5,      /* bad segment kind, lengths not summing to N, too many */
+    BSATTN_ERR_BUDGET = 6,      /* budget/density NaN or <= 0; bad head-mask args      */
+    BSATTN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required             */
+    BSATTN_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed          */
+    BSATTN_ERR_UNSUPPORTED = 9  /* valid request this build has no kernel for          */
+} bsattn_status;
+
+/* Element types of q, k, v and out. */
+typedef enum { BSATTN_BF16 = 0, BSATTN_F32 = 1 } bsattn_dtype;
+
+/*
+ * A device tensor viewed as [B][H][N][D].  Strides are in elements; the D
+ * axis must be contiguous (stride 1).  `data` must be 16-byte aligned and
+ * stride_n * element size must be a multiple of 16 bytes.
+ */
+typedef struct {
+    void* data;
+    int32_t dtype;              /* bsattn_dtype */
+    int64_t B, H, N, D;
+    int64_t stride_b, stride_h, stride_n;
+} bsattn_tensor;
+
+/*
+ * Token kinds of a packed sequence (SD.Next layout paragraph): image and
+ * video tokens are sparsifiable; text, conditioning, audio and anything else
+ * pin their block's rows and columns dense; padding blocks are dropped.
+ */
+typedef enum {
+    BSATTN_SEG_TEXT = 0,
+    BSATTN_SEG_CONDITIONING = 1,
+    BSATTN_SEG_AUDIO = 2,
+    BSATTN_SEG_OTHER = 3,
+    BSATTN_SEG_IMAGE = 4,
+    BSATTN_SEG_VIDEO = 5,
+    BSATTN_SEG_PADDING = 6
+} bsattn_seg_kind;
+
+typedef struct {
+    int32_t kind;               /* bsattn_seg_kind */
+    int64_t length;             /* tokens, > 0 */
+} bsattn_segment;
+
+#define BSATTN_MAX_SEGMENTS 32
+
+/*
+ * Token layout, read during the call only (host memory).
+ *  block         : tokens per block, 32 or 64.
+ *  n_segments    : 0..BSATTN_MAX_SEGMENTS.  0 = no layout: every block is
+ *                  sparsifiable (the whole sequence is sparsified).
+ *  segments      : ordered segments whose lengths sum to N.
+ *  window_tokens : 0 = none; otherwise a sliding window of total span W
+ *                  tokens: a pair of sparsifiable blocks is always kept when
+ *                  some query token and key token are at most W/2 apart.
+ * A block is DROPPED when all its tokens are padding, SPARSE when all its
+ * tokens lie in one image or video segment, PINNED otherwise (a block that
+ * straddles a segment boundary pins).
+ */
+typedef struct {
+    int32_t block;
+    int32_t n_segments;
+    const bsattn_segment* segments;
+    int32_t window_tokens;
+} bsattn_layout;
+
+/*
+ * Block mask in CSR-like form (glossary: CSR, row-wise).  Device buffers
+ * owned by the caller:
+ *   mask  uint8 [B][H][nqb][nkb]  1 = the (query block, key block) tile is kept
+ *   count int32 [B][H][nqb]       kept tiles per query block
+ *   index int32 [B][H][nqb][nkb]  kept key blocks in ascending order; only
+ *                                 the first count entries are written/valid
+ * B and H may be 1 to share one mask across batch entries or heads
+ * (bsattn_radial writes a single layout-only mask that way).
+ * is_dense and k are host out-fields, written synchronously by the call:
+ *   k        candidates kept per sparsifiable row
+ *   is_dense 1 when the budget covers every candidate (the layout-only mask
+ *            is written instead of a scored one).
+ */
+typedef struct {
+    int32_t B, H, nqb, nkb;
+    uint8_t* mask;
+    int32_t* count;
+    int32_t* index;
+    int32_t is_dense;
+    int32_t k;
+} bsattn_block_mask;
+
+/* Human-readable name of a status code (static storage). */
+const char* bsattn_status_string(bsattn_status st);
+
+/*
+ * Host-side geometry (SD.Next synchronisation paragraph: the parts that
+ * depend only on the layout are computed on the host, so no device value is
+ * ever read back).  classes[NB] receives 0 = SPARSE, 1 = PINNED,
+ * 2 = DROPPED for NB = N / layout->block blocks; *n_cand the number of
+ * SPARSE blocks.  No GPU needed.
+ */
+bsattn_status bsattn_layout_classes(const bsattn_layout* layout, int64_t N,
+                                    uint8_t* classes, int32_t* n_cand);
+
+/*
+ * Budget rule (SD.Next selector paragraph: a fraction of the sparsifiable
+ * candidates; a budget covering every candidate reports dense):
+ *   k = max(1, min(n_cand, floor(budget * n_cand + 1e-9))),
+ *   is_dense = (k >= n_cand); n_cand == 0 gives k = 0, is_dense = 1.
+ * budget must be finite and > 0.  No GPU needed.
+ */
+bsattn_status bsattn_budget_k(int32_t n_cand, double budget, int32_t* k, int32_t* is_dense);
+
+/*
+ * Workspace bytes bsattn_select needs (device memory, 256-byte aligned):
+ * fp32 block sums of Q and K for the sparsifiable blocks.  An upper bound
+ * that holds for every layout with these sizes.
+ */
+size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                     int32_t block, int64_t D);
+
+/*
+ * Content-aware selection (SD.Next selector + layout paragraphs).
+ *  q [B][H][N][D], k [B][Hkv][N][D] (Hkv divides H; query head h scores
+ *  against kv head h / (H / Hkv), no key expansion), same dtype, D in
+ *  {32, 64, 128}, N a multiple of layout->block.
+ *  For every (b, h) and every SPARSE query block i: block sums of Q and K,
+ *  unscaled scores S_ij = <sum Q_i, sum K_j> over SPARSE j (ranking equals
+ *  that of mean-pooled scores), keep the diagonal plus the k-1 best other
+ *  candidates (higher score first, ties to the lower block index), OR the
+ *  sliding window, then apply pins and drops.  PINNED rows keep every
+ *  non-dropped column; DROPPED rows and columns are empty.
+ *  out: B == q->B, H == q->H, nqb == nkb == N / block; mask, count and index
+ *  fully written.  out->k and out->is_dense are set before returning.
+ *  When is_dense, no scoring runs and the layout-only mask is written.
+ *  workspace: device, >= bsattn_select_workspace_bytes(...), 256-aligned.
+ *  Limits: number of sparsifiable blocks <= 2048.
+ *  Enqueues two kernels on `stream`; never synchronises.
+ */
+bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
+                            const bsattn_layout* layout, double budget,
+                            bsattn_block_mask* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Radial control (SD.Next radial-control paragraph): every SPARSE row keeps
+ * the k SPARSE candidates nearest the diagonal, ordered by (|i - j|, j), with
+ * k from the same budget rule applied to `density`; same window, pins and
+ * drops as bsattn_select.  N = out->nqb * layout->block.  The layout-only
+ * result is written to every (b, h) slice of out (out->B, out->H >= 1; use 1
+ * and 1 for one shared mask).  Enqueues one kernel; never synchronises.
+ */
+bsattn_status bsattn_radial(const bsattn_layout* layout, double density,
+                            bsattn_block_mask* out, void* stream);
+
+/*
+ * Block-sparse attention forward (SD.Next flex-consumer paragraph; glossary
+ * block-sparse entry; head masks from the haagenti_sparse crate).
+ *  q, out [B][H][N][D]; k, v [B][Hkv][N][D]; same dtype.
+ *  For each (b, h) with head_mask[h] != 0 and each query block i, the output
+ *  rows equal softmax(scale * Q_i K^T + M) V where M is 0 on the key blocks
+ *  listed in mask->index[b][h][i][0..count) and -inf elsewhere.  Rows with no
+ *  kept block, and all rows of heads with head_mask[h] == 0, are written as 0.
+ *  mask: nqb == nkb == N / block; mask->B in {1, B}, mask->H in {1, H};
+ *        only count and index are read.  NULL = every block kept (dense).
+ *  block: 64 when mask is NULL; otherwise N / mask->nqb, which must be 32
+ *        or 64.
+ *  head_mask: device uint8 [H], or NULL = every head active.
+ *  scale: <= 0 means 1/sqrt(D).
+ *  bf16 inputs use the MFMA path (block 64, D 64 or 128) with fp32 softmax
+ *  and one final rounding to bf16; fp32 inputs (and other bf16 shapes) use a
+ *  fp32 vector path.  Enqueues one kernel; never synchronises.
+ */
+bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
+                             const bsattn_tensor* v, const bsattn_block_mask* mask,
+                             const uint8_t* head_mask, float scale,
+                             bsattn_tensor* out, void* stream);
+
+/*
+ * Per-layer head mask (haagenti_sparse AttentionMask / MaskBuilder with
+ * DEFAULT_SPARSITY and MIN_ACTIVE_HEADS): skip floor(sparsity * H) heads but
+ * keep at least min(H, min_active); the kept heads are those with the highest
+ * importance, ties to the lower head index.  Host memory in and out
+ * (importance double[H], out uint8[H]).  sparsity in [0, 1], min_active >= 0.
+ * No GPU needed.
+ */
+bsattn_status bsattn_head_mask(const double* importance, int32_t H, double sparsity,
+                               int32_t min_active, uint8_t* out);
+
+/*
+ * Lazy density (SD.Next synchronisation paragraph: density is read back only
+ * when asked): kept tiles / (B * H * nqb * nkb).  Copies `count` to the host
+ * and SYNCHRONISES `stream`; not for the hot path.
+ */
+bsattn_status bsattn_mask_density(const bsattn_block_mask* m, void* stream, double* density);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

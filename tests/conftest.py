@@ -36,3 +36,11 @@ def cuda():
         pytest.fail("a GPU test ran without a visible GPU")
     import torch
     return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Name every GPU test on the real stderr before it touches the GPU."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"[gpu-test] start {request.node.nodeid}", file=sys.__stderr__, flush=True)
+    yield

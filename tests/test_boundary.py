@@ -1,0 +1,226 @@
+"""C-ABI boundary tests on the CPU: exports, host geometry, validation codes.
+
+No kernel is launched here: every call either is host-only or fails
+validation, which returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from head_masked_attention_amd import _binding as B_
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7f0000100000            # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsattn.h")).read()
+    return sorted(set(re.findall(r"\b(bsattn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B_.EXPORTS)
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        assert B_.status_string(s)
+    assert B_.status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("w", list(workloads.ALL.values()), ids=lambda w: w.name)
+def test_layout_classes_match_oracle_on_workloads(lib, w):
+    lay = B_.Layout(w.block, list(w.segments), w.window_tokens)
+    cls, n = B_.layout_classes(lay, w.N)
+    ref = oracle.classes(list(w.segments), w.N, w.block)
+    assert np.array_equal(cls, ref)
+    assert n == int((ref == 0).sum())
+
+
+def test_layout_classes_match_oracle_on_random_layouts(lib):
+    rng = np.random.default_rng(0)
+    kinds = list(B_.SEG_KINDS)
+    for trial in range(300):
+        block = int(rng.choice([32, 64]))
+        nseg = int(rng.integers(1, 12))
+        lens = rng.integers(1, 200, size=nseg)
+        N = int(lens.sum())
+        pad = (-N) % block
+        lens[-1] += pad
+        N += pad
+        segs = [(kinds[int(rng.integers(len(kinds)))], int(x)) for x in lens]
+        cls, n = B_.layout_classes(B_.Layout(block, segs), N)
+        ref = oracle.classes(segs, N, block)
+        assert np.array_equal(cls, ref), segs
+
+
+def test_budget_rule_matches_oracle(lib):
+    for n in [0, 1, 2, 7, 8, 63, 64, 256, 512, 2048]:
+        for b in [1e-6, 0.01, 0.1, 0.2, 0.25, 0.3, 1 / 3, 0.5, 0.7, 0.99, 1.0, 1.5, 7.0]:
+            assert B_.budget_k(n, b) == oracle.budget(n, b), (n, b)
+    # the workloads' k values
+    assert B_.budget_k(8, 0.5) == (4, False)
+    assert B_.budget_k(64, 0.3)[0] == 19 and B_.budget_k(256, 0.3)[0] == 76
+    assert B_.budget_k(512, 0.3)[0] == 153 and B_.budget_k(63, 0.3)[0] == 18
+
+
+def test_head_mask_matches_oracle(lib):
+    rng = np.random.default_rng(1)
+    for trial in range(200):
+        H = int(rng.integers(1, 40))
+        imp = rng.integers(0, 5, size=H).astype(float) if trial % 2 else rng.random(H)
+        sp = float(rng.choice([0.0, 0.25, 0.5, 0.75, 1.0]))
+        mn = int(rng.integers(0, 6))
+        assert np.array_equal(B_.head_mask(imp, sp, mn), oracle.head_mask(imp, sp, mn))
+    for layer in (0, 21, 42, 63):
+        imp = workloads.head_importance(workloads.STACK, layer)
+        m = B_.head_mask(imp)
+        assert m.sum() == 16 and np.array_equal(m, oracle.head_mask(imp, 0.5, 4))
+
+
+# ----- validation codes --------------------------------------------------------
+
+def tensor(B=1, H=2, N=256, D=64, dtype=B_.BF16, data=FAKE, sn=None, sh=None, sb=None):
+    sn = D if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return B_._Tensor(data, dtype, B, H, N, D, sb, sh, sn)
+
+
+def bmask(B=1, H=2, nb=4, null=False):
+    return B_._BlockMask(B, H, nb, nb, 0 if null else FAKE, FAKE, FAKE, -7, -7)
+
+
+def layout(block=64, segs=(), window=0):
+    lay, keep = B_.Layout(block, list(segs), window)._c()
+    return lay, keep
+
+
+def call_select(lib, q, k, lay, budget, out, ws=FAKE, ws_bytes=1 << 30):
+    return lib.bsattn_select(ctypes.byref(q), ctypes.byref(k), ctypes.byref(lay), budget,
+                             ctypes.byref(out), ws, ws_bytes, None)
+
+
+def test_select_validation(lib):
+    lay, _k = layout()
+    q, k = tensor(), tensor()
+    cases = [
+        (dict(q=tensor(data=0)), 1),
+        (dict(q=tensor(dtype=5)), 2),
+        (dict(k=tensor(dtype=B_.F32)), 2),
+        (dict(q=tensor(D=48)), 3),
+        (dict(q=tensor(N=250, sn=64)), 3),
+        (dict(k=tensor(H=3)), 3),
+        (dict(q=tensor(data=FAKE + 2)), 4),
+        (dict(q=tensor(sn=60)), 4),
+        (dict(out=bmask(null=True)), 1),
+        (dict(out=bmask(nb=5)), 3),
+        (dict(out=bmask(H=1)), 3),
+        (dict(budget=0.0), 6),
+        (dict(budget=float("nan")), 6),
+        (dict(budget=-1.0), 6),
+        (dict(ws=0), 7),
+        (dict(ws_bytes=100), 7),
+        (dict(ws=FAKE + 16), 7),
+    ]
+    for over, code in cases:
+        args = dict(q=q, k=k, lay=lay, budget=0.3, out=bmask(), ws=FAKE, ws_bytes=1 << 30)
+        args.update(over)
+        out = args["out"]
+        st = call_select(lib, args["q"], args["k"], args["lay"], args["budget"], out,
+                         args["ws"], args["ws_bytes"])
+        assert st == code, (over, st)
+        assert out.k == -7 and out.is_dense == -7          # untouched on error
+
+
+def test_select_layout_errors(lib):
+    q, k = tensor(), tensor()
+    for segs, code in [([("text", 100)], 5), ([("image", 128), ("text", 100)], 5),
+                       ([("image", 256), ("padding", 0)], 5), ([(9, 256)], 5)]:
+        lay, _k = layout(segs=segs)
+        assert call_select(lib, q, k, lay, 0.3, bmask()) == code
+    lay, _k = layout(block=48)
+    assert call_select(lib, q, k, lay, 0.3, bmask()) == 3
+    too_many = [("image", 8)] * 32 + [("text", 0)]
+    lay, _k = layout(segs=too_many)
+    assert call_select(lib, q, k, lay, 0.3, bmask()) == 5
+    lay, _k = layout(window=-1)
+    assert call_select(lib, q, k, lay, 0.3, bmask()) == 5
+
+
+def test_select_unsupported_candidate_count(lib):
+    N = 64 * 2100
+    q, k = tensor(N=N, D=32), tensor(N=N, D=32)
+    lay, _k = layout()
+    assert call_select(lib, q, k, lay, 0.3, bmask(nb=2100)) == 9
+
+
+def call_forward(lib, q, k, v, m, out, scale=0.0):
+    return lib.bsattn_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                              None if m is None else ctypes.byref(m), None, scale,
+                              ctypes.byref(out), None)
+
+
+def test_forward_validation(lib):
+    cases = [
+        (dict(q=tensor(data=0)), 1),
+        (dict(v=tensor(dtype=B_.F32)), 2),
+        (dict(out=tensor(dtype=B_.F32)), 2),
+        (dict(k=tensor(N=128)), 3),
+        (dict(v=tensor(H=1)), 3),
+        (dict(out=tensor(D=32)), 3),
+        (dict(m=bmask(nb=3)), 3),              # 256 / 3 not integral
+        (dict(m=bmask(nb=16)), 3),             # block 16 unsupported
+        (dict(m=bmask(B=2)), 3),
+        (dict(m=B_._BlockMask(1, 2, 4, 4, FAKE, 0, FAKE, 0, 0)), 1),
+        (dict(scale=float("inf")), 6),
+        (dict(q=tensor(sn=72, sh=256 * 72 + 4)), 4),
+    ]
+    for over, code in cases:
+        args = dict(q=tensor(), k=tensor(), v=tensor(), m=bmask(), out=tensor(), scale=0.0)
+        args.update(over)
+        st = call_forward(lib, args["q"], args["k"], args["v"], args["m"], args["out"], args["scale"])
+        assert st == code, (over, st)
+
+
+def test_radial_and_density_validation(lib):
+    lay, _k = layout()
+    out = bmask()
+    assert lib.bsattn_radial(ctypes.byref(lay), 0.0, ctypes.byref(out), None) == 6
+    assert lib.bsattn_radial(None, 0.3, ctypes.byref(out), None) == 1
+    bad = bmask(nb=4)
+    bad.nkb = 5
+    assert lib.bsattn_radial(ctypes.byref(lay), 0.3, ctypes.byref(bad), None) == 3
+    d = ctypes.c_double()
+    assert lib.bsattn_mask_density(None, None, ctypes.byref(d)) == 1
+    z = bmask()
+    z.B = 0
+    assert lib.bsattn_mask_density(ctypes.byref(z), None, ctypes.byref(d)) == 3
+
+
+def test_head_mask_validation(lib):
+    imp = np.zeros(4)
+    out = np.zeros(4, np.uint8)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.bsattn_head_mask(None, 4, 0.5, 4, p(out)) == 1
+    assert lib.bsattn_head_mask(p(imp), 0, 0.5, 4, p(out)) == 3
+    assert lib.bsattn_head_mask(p(imp), 4, 1.5, 4, p(out)) == 6
+    assert lib.bsattn_head_mask(p(imp), 4, 0.5, -1, p(out)) == 6
+    imp[2] = np.nan
+    assert lib.bsattn_head_mask(p(imp), 4, 0.5, 4, p(out)) == 6
+
+
+def test_workspace_bytes(lib):
+    assert B_.select_workspace_bytes(2, 10, 10, 4096, 64, 64) == 2 * 2 * 10 * 64 * 64 * 4
+    assert B_.select_workspace_bytes(1, 4, 2, 512, 32, 32) == 256 * ((4 * 16 * 32 * 4 + 255) // 256) + \
+        256 * ((2 * 16 * 32 * 4 + 255) // 256)
+    assert B_.select_workspace_bytes(1, 1, 1, 512, 48, 32) == 0

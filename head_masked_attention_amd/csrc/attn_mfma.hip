@@ -2,17 +2,25 @@
 //
 // One workgroup of two wavefronts per (b, h, 64-token query block); each
 // wavefront owns 32 query rows.  The workgroup walks the compacted list of
-// kept key blocks (CSR-like, ascending), stages each 64-key K and V tile in
-// LDS, and runs
-//     S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, Q^T fragments held in VGPRs)
-//     online softmax in fp32 (exp2 with the scale folded into log2 units)
-//     O^T += V^T P^T (V^T fragments read with ds_read_b64_tr_b16)
-// so that every lane holds one query's scores and one query's output column
-// and the softmax statistics never leave the lane pair (lane, lane ^ 32).
-// The K rows are loaded into MFMA row slots in a fixed permutation chosen so
-// that each lane's eight P values of a 16-key step are consecutive keys, which
-// is exactly the B-operand layout of the P V product: no shuffle of P.
-// Masked heads and rows without kept blocks write zeros and exit.
+// kept key blocks (CSR-like, ascending) in stages of KT keys:
+//   - K and V stage tiles go from HBM/L2 straight into LDS with
+//     global_load_lds_dwordx4 (no register staging), NST stages deep, one
+//     barrier per stage;
+//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the Q^T fragments held in
+//     VGPRs for the whole loop;
+//   - online softmax in fp32: exp2 with the scale folded into log2 units, and
+//     the running output rescaled only when a row maximum grows by more than
+//     2^8 (exponentials stay <= 256, exact after the final division);
+//   - O^T += V^T P^T with the V^T fragments read by ds_read_b64_tr_b16 from
+//     the row-major V tile, so V is never transposed in memory.
+// Every lane holds one query's scores and one query's output column; the
+// softmax statistics of a row live in the lane pair (lane, lane ^ 32).  K rows
+// feed the MFMA row slots in a fixed permutation so that each lane's eight P
+// values of a 16-key step are consecutive keys — the B-operand layout of the
+// P V product — so P never moves between lanes.
+// LDS tiles use an XOR swizzle of 16-byte chunks, chosen so that both the
+// 16-byte K fragment reads and the transposing V reads are free of bank
+// conflicts.  Masked heads and rows without kept blocks write zeros and exit.
 //
 // Sources: SD.Next commit view, modules/attention/sparse, flex-consumer
 // paragraph (only the selected tiles are computed); inferensys glossary,
@@ -28,10 +36,23 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef short s4v __attribute__((ext_vector_type(4)));
 typedef short s8v __attribute__((ext_vector_type(8)));
 
+constexpr int kListMax = 1024;     // kept-block indices staged in LDS per workgroup
+
 // MFMA row slot -> key within a 32-key tile.
 __device__ __forceinline__ int slot_key(int s) {
     const int q = s >> 3, hh = (s >> 2) & 1, r = s & 3;
     return 16 * (q >> 1) + 8 * hh + 4 * (q & 1) + r;
+}
+
+// XOR swizzle of the 16-byte chunks of LDS row r (see the header comment).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    if constexpr (D == 64) {
+        const int m = (r >> 1) & 7;
+        return ((m & 1) << 2) | (m >> 1);
+    } else {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -39,17 +60,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void attn_mfma_kernel(AttnArgs a) {
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D, int KT, int NST>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
-    constexpr int KS = D + 8;      // K tile row stride (bf16): conflict-free 16-byte row reads
-    constexpr int VS = D + 32;     // V tile row stride (bf16): conflict-free transpose reads
-    constexpr int CPR = D / 8;     // 16-byte chunks per row
-    constexpr int NCH = BLK * CPR / 128;   // chunks per thread per tile
-    constexpr int NKS = D / 16;    // k-steps of S^T
-    constexpr int NDT = D / 32;    // d tiles of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[BLK * VS];
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int NI = KT * CPR / 128;       // loads per thread per tensor per stage
+    constexpr int TILE_ELEMS = KT * D;       // bf16 elements per K (or V) stage tile
+    constexpr int NKT = KT / 32;             // 32-key S^T tiles per stage
+    constexpr int NKS = D / 16;              // k-steps of S^T
+    constexpr int NDT = D / 32;              // 32-row d tiles of O^T
+    constexpr int NPS = KT / 16;             // 16-key steps of O^T per stage
+    constexpr int SUB = BLK / KT;            // stages per key block
+    constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
+    static_assert(NI >= 1 && KT * CPR % 128 == 0, "stage tiling");
+
+    // one LDS object per stage: distinct objects let the compiler see that the
+    // reads of one stage never alias the loads in flight into the other
+    __shared__ __attribute__((aligned(16))) uint16_t K0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t V0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t K1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t V1[TILE_ELEMS];
+    __shared__ int32_t s_list[kListMax];
+    static_assert(NST == 2, "two LDS stages");
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
@@ -74,13 +114,15 @@ __global__ __launch_bounds__(128) void attn_mfma_kernel(AttnArgs a) {
 
     if (!active || cnt <= 0) {
         const uint4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const int c = tid + 128 * t;
+        for (int c = tid; c < BLK * CPR; c += 128)
             *(uint4*)(obase + (int64_t)(c / CPR) * a.o_sn + (c % CPR) * 8) = z;
-        }
         return;
     }
+
+    // kept-block list into LDS (beyond kListMax the tail is read from memory)
+    const bool list_in_lds = list != nullptr && cnt <= kListMax;
+    if (list_in_lds)
+        for (int i = tid; i < cnt; i += 128) s_list[i] = list[i];
 
     const uint16_t* qbase = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qb * BLK * a.q.sn;
     const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.sb + kvh * a.k.sh;
@@ -93,19 +135,42 @@ __global__ __launch_bounds__(128) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
     }
+    __syncthreads();   // s_list visible
 
-    uint4 kreg[NCH], vreg[NCH];
-    auto prefetch = [&](int32_t kb) {
-        const uint16_t* kt = kbase + (int64_t)kb * BLK * a.k.sn;
-        const uint16_t* vt = vbase + (int64_t)kb * BLK * a.v.sn;
+    const int T = cnt * SUB;   // stages
+    auto block_of = [&](int t) -> int32_t {
+        const int i = t / SUB;
+        if (list == nullptr) return i;
+        return list_in_lds ? s_list[i] : list[i];
+    };
+    // per-thread source offsets of the NI chunks it loads per stage: LDS chunk
+    // slot s = i*128 + tid holds row s / CPR, global chunk (s % CPR) ^ swizzle
+    int32_t koff[NI], voff[NI];
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const int c = tid + 128 * t;
-            kreg[t] = *(const uint4*)(kt + (int64_t)(c / CPR) * a.k.sn + (c % CPR) * 8);
-            vreg[t] = *(const uint4*)(vt + (int64_t)(c / CPR) * a.v.sn + (c % CPR) * 8);
+    for (int i = 0; i < NI; ++i) {
+        const int s = i * 128 + tid;
+        const int r = s / CPR;
+        const int c = (s % CPR) ^ chunk_swizzle<D>(r);
+        koff[i] = r * (int32_t)a.k.sn + c * 8;
+        voff[i] = r * (int32_t)a.v.sn + c * 8;
+    }
+    // issue the K and V loads of stage t into LDS buffer (Kd, Vd)
+    auto issue = [&](int t, uint16_t* Kd, uint16_t* Vd) {
+        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+        const uint16_t* kt = kbase + row0 * a.k.sn;
+        const uint16_t* vt = vbase + row0 * a.v.sn;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int dst = (i * 128 + wave * 64) * 8;   // wave-uniform element offset
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(kt + koff[i]),
+                (__attribute__((address_space(3))) void*)(Kd + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(vt + voff[i]),
+                (__attribute__((address_space(3))) void*)(Vd + dst), 16, 0, 0);
         }
     };
-    prefetch(list ? list[0] : 0);
+    issue(0, K0, V0);
 
     const float sl2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
     float m_run = -INFINITY, l_run = 0.f;
@@ -115,86 +180,90 @@ __global__ __launch_bounds__(128) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
 
-    const int krow = slot_key(ql);   // K row this lane feeds into MFMA row slot ql
     const int g16 = lane >> 4, j16 = lane & 15;
 
-    for (int32_t it = 0; it < cnt; ++it) {
+    // one stage: wait for its tiles, make them visible, start the next
+    // stage's loads into the other buffers, then compute from this one
+    auto stage = [&](int t, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
+        wait_vmcnt<0>();
         __syncthreads();
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const int c = tid + 128 * t;
-            *(uint4*)(Ks + (c / CPR) * KS + (c % CPR) * 8) = kreg[t];
-            *(uint4*)(Vs + (c / CPR) * VS + (c % CPR) * 8) = vreg[t];
-        }
-        __syncthreads();
-        if (it + 1 < cnt) prefetch(list ? list[it + 1] : it + 1);
+        if (t + 1 < T) issue(t + 1, Kn, Vn);
 
-        // S^T for two 32-key tiles
-        f16v sacc[2];
+        // S^T for NKT 32-key tiles
+        f16v sacc[NKT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-            const uint16_t* kr = Ks + (32 * kt + krow) * KS + 8 * hl;
+            const int r = 32 * kt + slot_key(ql);
+            const int sw = chunk_swizzle<D>(r);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 kf = *(const bf16x8*)(kr + 16 * ks);
+                const bf16x8 kf = *(const bf16x8*)(Kt + (r * CPR + ((2 * ks + hl) ^ sw)) * 8);
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
             }
         }
 
-        // online softmax (lane: query 32*wave + ql; keys split with lane ^ 32)
+        // online softmax with lazy rescaling
         float mx = sacc[0][0];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        const bool grow = mx > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
+            const float m_new = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
 
-        bf16x8 pf[4];   // B operand of P V for the four 16-key steps
+        bf16x8 pf[NPS];   // B operand of P V, one per 16-key step
         float psum = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_new));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_new));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_run));
                     psum += p0 + p1;
                     w[e >> 1] = pack_bf16x2(p0, p1);
                 }
                 pf[2 * kt + u] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        l_run += psum;
 
-        // O^T += V^T P^T: V^T fragments via transpose reads of the row-major tile.
-        // Within each 16-lane group, lane j supplies V[kb + j/4][d0 + 4*(j%4)];
-        // lane i then receives V[kb + 0..3][d0 + i].
+        // O^T += V^T P^T.  Within each 16-lane group, lane j supplies
+        // V[kb + j/4][d0 + 4*(j%4) .. +3]; lane i then receives V[kb + 0..3][d0 + i].
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const int d0 = 32 * dt + 16 * (g16 & 1);
+            const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
+            const int c = d >> 3, half = (d >> 2) & 1;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kb0 = 16 * ks + 8 * hl;
-                const uint16_t* p0 = Vs + (kb0 + (j16 >> 2)) * VS + d0 + 4 * (j16 & 3);
-                const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s4v*)(p0));
-                const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s4v*)(p0 + 4 * VS));
+            for (int ks = 0; ks < NPS; ++ks) {
+                const int r0 = 16 * ks + 8 * hl + (j16 >> 2);
+                const int r1 = r0 + 4;
+                const uint16_t* p0 = Vt + (r0 * CPR + (c ^ chunk_swizzle<D>(r0))) * 8 + half * 4;
+                const uint16_t* p1 = Vt + (r1 * CPR + (c ^ chunk_swizzle<D>(r1))) * 8 + half * 4;
+                const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p0));
+                const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p1));
                 const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[ks],
                                                                   oacc[dt], 0, 0, 0);
             }
         }
+    };
+    for (int t = 0; t < T; t += 2) {
+        stage(t, K0, V0, K1, V1);
+        if (t + 1 < T) stage(t + 1, K1, V1, K0, V0);
     }
 
     // normalise and store: oacc[dt][r] = O[query][32*dt + 8*(r/4) + 4*hl + r%4]
@@ -215,8 +284,8 @@ __global__ __launch_bounds__(128) void attn_mfma_kernel(AttnArgs a) {
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {
     const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
     const dim3 grid((unsigned)padded);
-    if (D == 128) hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(128), 0, s, a);
+    if (D == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, 32, 2>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_mfma_kernel<64, 64, 2>), grid, dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

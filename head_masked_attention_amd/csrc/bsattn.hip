@@ -300,8 +300,11 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
 
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (q->dtype == BSATTN_BF16 && block == 64 && (q->D == 64 || q->D == 128))
+    if (q->dtype == BSATTN_BF16 && block == 64 && (q->D == 64 || q->D == 128)) {
+        // the MFMA kernel keeps per-thread K/V row offsets of one block in 32 bits
+        if (k->stride_n > (1 << 24) || v->stride_n > (1 << 24)) return BSATTN_ERR_UNSUPPORTED;
         e = launch_attn_mfma(a, (int)q->D, s);
+    }
     else
         e = launch_attn_vec(a, q->dtype == BSATTN_F32, (int)q->D, (int)block, s);
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;

@@ -213,7 +213,8 @@ bsattn_status bsattn_radial(const bsattn_layout* layout, double density,
  *        or 64.
  *  head_mask: device uint8 [H], or NULL = every head active.
  *  scale: <= 0 means 1/sqrt(D).
- *  bf16 inputs use the MFMA path (block 64, D 64 or 128) with fp32 softmax
+ *  bf16 inputs use the MFMA path (block 64, D 64 or 128; K/V stride_n <= 2^24)
+ *  with fp32 softmax
  *  and one final rounding to bf16; fp32 inputs (and other bf16 shapes) use a
  *  fp32 vector path.  Enqueues one kernel; never synchronises.
  */

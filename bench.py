@@ -34,6 +34,34 @@ import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
+ATTN_SOURCES = ["head_masked_attention_amd/csrc/attn_mfma.hip", "head_masked_attention_amd/csrc/common.h",
+                "head_masked_attention_amd/csrc/internal.h"]
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_mfma_kernel__{workload}__hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith(("kernel_source_sha256", "traffic_bytes_per_launch")):
+                k, v = line.strip().split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != attn_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in vals else None
 
 
 def parse():
@@ -122,33 +150,33 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # whole-step throughput: K steps (select + forward), host clock, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream)
-        ev[i][1].record(stream)
-        hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=stream)
-        ev[i][2].record(stream)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
 
+    def timed_launches(fn):
+        """Average launch time of fn over K back-to-back launches, HIP events
+        recorded on the stream the kernels run on."""
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    sel_ms = timed_launches(lambda: hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream))
+    fwd_ms = timed_launches(lambda: hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=stream))
     # the same attention kernel at full density (budget 1.0: same layout and head mask)
     hm.select(qd, kd, layout, 1.0, out=bm_full, workspace=ws, stream=stream)
-    for _ in range(args.warmup):
-        hm.forward(qd, kd, vd, bm_full, head_mask, out=out, stream=stream)
-    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        evd[i][0].record(stream)
-        hm.forward(qd, kd, vd, bm_full, head_mask, out=out, stream=stream)
-        evd[i][1].record(stream)
-    torch.cuda.synchronize()
-    dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evd]))
+    dense_ms = timed_launches(lambda: hm.forward(qd, kd, vd, bm_full, head_mask, out=out, stream=stream))
 
     # the step's own result, outside every timed region
     hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream)
@@ -164,10 +192,12 @@ def main():
         cpu = cpu_baseline(w, q, k, v, list(w.segments), head_mask_np, flops)
 
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        # an elementwise kernel that reads 256 MiB and writes 256 MiB: the known
+        # byte count that scales the HBM fetch/write counters
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
     res = {
@@ -190,7 +220,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel" if w.dtype == "bf16" else "attn_vec_kernel",
                      "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(w.name),
+                     "traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
                      "flops_per_launch": flops, "avg_launch_ms": fwd_ms},
         "selector": {"bound": "hbm", "achieved": sel_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": sel_gbps / HBM_PEAK_GBPS, "bytes_per_call": sel_bytes, "avg_call_ms": sel_ms},

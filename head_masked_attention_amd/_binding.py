@@ -71,6 +71,9 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing; build it with head_masked_attention_amd.build.build()")
+    # torch ships its own HIP runtime under the same soname: load it first so
+    # libbsattn binds to that one and torch's streams are valid in our calls
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double

@@ -35,6 +35,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef short s4v __attribute__((ext_vector_type(4)));
 typedef short s8v __attribute__((ext_vector_type(8)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
 constexpr int kListMax = 1024;     // kept-block indices staged in LDS per workgroup
 
@@ -55,9 +57,12 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
     }
 }
 
+// Two floats to packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf2v to_bf16x2(float lo, float hi) {
+    return __builtin_convertvector((f2v){lo, hi}, bf2v);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
@@ -67,8 +72,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int KT, int NST>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// ROWSUM_MFMA: the softmax denominators come from one extra O^T tile whose
+// A operand is all ones (the MFMA pipe sums the bf16 P it multiplies);
+// otherwise the VALU sums packed P with bf16 dot products.
+template <int D, int KT, int NST, bool ROWSUM_MFMA, int WPE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
     constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -175,10 +183,15 @@ void attn_mfma_kernel(AttnArgs a) {
     const float sl2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
     float m_run = -INFINITY, l_run = 0.f;
     f16v oacc[NDT];
+    f16v lacc;                                          // row sums (ROWSUM_MFMA)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
     const int g16 = lane >> 4, j16 = lane & 15;
 
@@ -221,23 +234,31 @@ void attn_mfma_kernel(AttnArgs a) {
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            if constexpr (ROWSUM_MFMA)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
         }
 
         bf16x8 pf[NPS];   // B operand of P V, one per 16-key step
         float psum = 0.f;
+        const bf2v one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                uint32_t w[4];
+                bf2v w[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_run));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_run));
-                    psum += p0 + p1;
-                    w[e >> 1] = pack_bf16x2(p0, p1);
+                    w[e >> 1] = to_bf16x2(p0, p1);
+                    if constexpr (!ROWSUM_MFMA) psum = __builtin_amdgcn_fdot2_f32_bf16(w[e >> 1], one2, psum, false);
                 }
-                pf[2 * kt + u] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+                pf[2 * kt + u] = __builtin_bit_cast(
+                    bf16x8, (uint4){__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
+                                    __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3])});
+                if constexpr (ROWSUM_MFMA)
+                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[2 * kt + u], lacc, 0, 0, 0);
             }
         l_run += psum;
 
@@ -267,7 +288,8 @@ void attn_mfma_kernel(AttnArgs a) {
     }
 
     // normalise and store: oacc[dt][r] = O[query][32*dt + 8*(r/4) + 4*hl + r%4]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // every row of the ones tile holds the full sum of the bf16 P of this query
+    const float l_tot = ROWSUM_MFMA ? lacc[0] : l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
     uint16_t* orow = obase + (int64_t)(32 * wave + ql) * a.o_sn;
 #pragma unroll
@@ -281,12 +303,34 @@ void attn_mfma_kernel(AttnArgs a) {
         }
 }
 
+// Launch shapes (keys per LDS stage, row-sum mode, waves per EU) per head dim.
+#ifndef BSATTN_D64_KT
+#define BSATTN_D64_KT 32
+#endif
+#ifndef BSATTN_D64_ROWSUM_MFMA
+#define BSATTN_D64_ROWSUM_MFMA false
+#endif
+#ifndef BSATTN_D64_WPE
+#define BSATTN_D64_WPE 3
+#endif
+#ifndef BSATTN_D128_KT
+#define BSATTN_D128_KT 32
+#endif
+#ifndef BSATTN_D128_ROWSUM_MFMA
+#define BSATTN_D128_ROWSUM_MFMA false
+#endif
+#ifndef BSATTN_D128_WPE
+#define BSATTN_D128_WPE 2
+#endif
+
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {
     const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
     const dim3 grid((unsigned)padded);
-    if (D == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, 32, 2>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<64, 64, 2>), grid, dim3(128), 0, s, a);
-    return hipGetLastError();
+    if (D == 128)
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, 2, BSATTN_D128_ROWSUM_MFMA, BSATTN_D128_WPE>, grid,
+                      dim3(128), s, a);
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, 2, BSATTN_D64_ROWSUM_MFMA, BSATTN_D64_WPE>, grid, dim3(128),
+                  s, a);
 }
 
 }  // namespace bsattn

@@ -113,9 +113,8 @@ template <typename T, int D>
 static hipError_t launch_vec_t(const AttnArgs& a, int block, hipStream_t s) {
     const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
     const dim3 grid((unsigned)padded);
-    if (block == 64) hipLaunchKernelGGL((attn_vec_kernel<T, D, 64>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((attn_vec_kernel<T, D, 32>), grid, dim3(32), 0, s, a);
-    return hipGetLastError();
+    if (block == 64) return launch(attn_vec_kernel<T, D, 64>, grid, dim3(64), s, a);
+    return launch(attn_vec_kernel<T, D, 32>, grid, dim3(32), s, a);
 }
 
 hipError_t launch_attn_vec(const AttnArgs& a, int dtype_is_f32, int D, int block, hipStream_t s) {

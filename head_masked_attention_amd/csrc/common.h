@@ -10,6 +10,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace bsattn {
 
 enum BlockClass : int32_t { CLS_SPARSE = 0, CLS_PINNED = 1, CLS_DROPPED = 2 };
@@ -93,6 +96,19 @@ __device__ __forceinline__ int64_t xcd_logical_id(int64_t w, int64_t padded) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
+}
+
+// Launches `kernel` and returns the status of this launch itself (not an
+// error left pending by earlier, unrelated runtime calls).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args&&... args) {
+    std::tuple<std::decay_t<KArgs>...> vals(std::forward<Args>(args)...);
+    void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto&... v) {
+        size_t i = 0;
+        ((ptrs[i++] = (void*)&v), ...);
+    }, vals);
+    return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s);
 }
 
 }  // namespace bsattn

@@ -166,21 +166,78 @@ __device__ __forceinline__ void compact_row(const Geometry& g, int lane, bool ro
     if (lane == 0) *cnt_out = cnt;
 }
 
+// Descending bitonic sort of R independent rows of 64*E 32-bit keys, one
+// wavefront per row set; element e = lane * E + r of row q lives in key[q][r].
+// The R networks are interleaved so their shuffles overlap.
+template <int R, int E>
+__device__ __forceinline__ void wave_bitonic_desc32(uint32_t (&key)[R][E], int lane) {
+    constexpr int NTOT = 64 * E;
+#pragma unroll
+    for (int size = 2; size <= NTOT; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride < E) {
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+#pragma unroll
+                    for (int r = 0; r < E; ++r) {
+                        if (r & stride) continue;
+                        const bool desc = ((lane * E + r) & size) == 0;
+                        const uint32_t a = key[q][r], b = key[q][r | stride];
+                        const uint32_t hi = max(a, b), lo = min(a, b);
+                        key[q][r] = desc ? hi : lo;
+                        key[q][r | stride] = desc ? lo : hi;
+                    }
+            } else {
+                const int lm = stride / E;
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+#pragma unroll
+                    for (int r = 0; r < E; ++r) {
+                        const int e = lane * E + r;
+                        const uint32_t other = __shfl_xor(key[q][r], lm);
+                        const bool take_max = ((e & stride) == 0) == ((e & size) == 0);
+                        key[q][r] = take_max ? max(key[q][r], other) : min(key[q][r], other);
+                    }
+            }
+        }
+    }
+}
+
+// Rows per workgroup and wavefronts per workgroup of the score/rank kernel.
+template <int E>
+struct RankShape {
+    static constexpr int RT = (E <= 2) ? 16 : (E <= 8 ? 32 : 16);
+    static constexpr int WAVES = (E <= 2) ? 4 : 8;
+};
+
 // ---------------------------------------------------------------------------
 // K2: scores, rank and compaction for one (b, h) and RT candidate rows.
 // The workgroup also writes its share of the PINNED/DROPPED rows.
+//
+// Rank keys.  Up to 512 candidates (E <= 8) a key is 32 bits: the
+// order-preserving image of the fp32 score with its low log2(64*E) bits
+// replaced by the reversed candidate position.  The kept bits resolve scores
+// to better than 2^-14 relative (6.1e-5): two scores that differ by more than
+// that always keep their order, so every row whose last kept and first
+// dropped scores differ by more than the 1e-4 near-tie window ranks exactly
+// as the exact ordering would, and closer scores fall to the lower block
+// index.  Larger candidate sets use 64-bit keys (full score, then position).
 // ---------------------------------------------------------------------------
 template <int D, int E>
-__global__ __launch_bounds__(256) void score_rank_kernel(const float* __restrict__ qp,
-                                                         const float* __restrict__ kp, int B,
-                                                         int H, int Hkv, Geometry g, MaskOut out,
-                                                         int n_tiles) {
+__global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
+    const float* __restrict__ qp, const float* __restrict__ kp, int B, int H, int Hkv, Geometry g,
+    MaskOut out, int n_tiles) {
     constexpr int NPAD = 64 * E;
-    constexpr int RT = (E <= 8) ? 32 : 16;     // candidate rows per workgroup
+    constexpr int RT = RankShape<E>::RT;
+    constexpr int WAVES = RankShape<E>::WAVES;
+    constexpr bool K32 = E <= 8;
+    constexpr int RPW = RT / WAVES;            // rows per wavefront
     constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
     constexpr int KQ = D / 4;                  // MFMA k-steps; lane group gq owns d in [gq*KQ, gq*KQ+KQ)
+    static_assert(RPW >= 1 && (!K32 || RPW % 2 == 0), "rows per wavefront");
     __shared__ float s_score[RT * SSTR];
-    __shared__ uint8_t s_keep[4][NPAD];
+    __shared__ uint8_t s_keep[WAVES][K32 ? 2 : 1][NPAD];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tile = blockIdx.x % n_tiles;
@@ -204,12 +261,19 @@ __global__ __launch_bounds__(256) void score_rank_kernel(const float* __restrict
         for (int c = 0; c < KQ / 4; ++c) a[rt][c] = src[c];
     }
     const int n_ct = (g.n_cand + 15) / 16;
-    for (int ct = wave; ct < n_ct; ct += 4) {
+    auto load_b = [&](int ct, f4v (&bv)[KQ / 4]) {
         const int jc = min(ct * 16 + li, g.n_cand - 1);
         const f4v* src = (const f4v*)(kbase + (int64_t)jc * D + gq * KQ);
-        f4v bv[KQ / 4];
 #pragma unroll
         for (int c = 0; c < KQ / 4; ++c) bv[c] = src[c];
+    };
+    f4v bnext[KQ / 4];
+    if (wave < n_ct) load_b(wave, bnext);
+    for (int ct = wave; ct < n_ct; ct += WAVES) {
+        f4v bv[KQ / 4];
+#pragma unroll
+        for (int c = 0; c < KQ / 4; ++c) bv[c] = bnext[c];
+        if (ct + WAVES < n_ct) load_b(ct + WAVES, bnext);
 #pragma unroll
         for (int rt = 0; rt < RT / 16; ++rt) {
             f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -227,10 +291,60 @@ __global__ __launch_bounds__(256) void score_rank_kernel(const float* __restrict
 
     const int64_t slice = b * H + h;
     const int64_t nb = g.nb;
-    // ---- per row: bitonic rank, keep the first k, compact
-    for (int r0 = 0; r0 < RT; r0 += 4) {
-        const int rl = r0 + wave;
-        if (rl < rows) {
+    const int32_t w = g.w;
+    auto compact_sparse = [&](int p, const uint8_t* keep_row) {
+        const int32_t i = cand_block(g, p);
+        compact_row(g, lane, false, false, out.mask + (slice * nb + i) * nb,
+                    out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
+                    [&](int32_t j, int32_t code) {
+                        return keep_row[code] != 0 || (w >= 0 && abs(j - i) <= w);
+                    });
+    };
+
+    if constexpr (K32) {
+        // ---- two rows at a time per wavefront
+        constexpr int IB = __builtin_ctz(NPAD);            // index bits
+        constexpr uint32_t IMASK = (1u << IB) - 1u;
+        for (int r0 = wave * RPW; r0 < wave * RPW + RPW; r0 += 2) {
+            uint32_t key[2][E];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int rl = r0 + q;
+                const int p = p0 + rl;
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int pos = lane * E + r;
+                    const uint32_t low = IMASK - (uint32_t)pos;
+                    uint32_t kv;
+                    if (rl >= rows || pos >= g.n_cand) kv = 0u;
+                    else if (pos == p) kv = (0xffffffffu << IB) | low;
+                    else kv = (orderable(s_score[rl * SSTR + pos]) & ~IMASK) | low;
+                    key[q][r] = kv;
+                }
+            }
+            wave_bitonic_desc32<2, E>(key, lane);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < E; ++r) s_keep[wave][q][lane * E + r] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < E; ++r)
+                    if (lane * E + r < g.k && r0 + q < rows) s_keep[wave][q][IMASK - (key[q][r] & IMASK)] = 1;
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                if (r0 + q < rows) compact_sparse(p0 + r0 + q, s_keep[wave][q]);
+            __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+        // ---- 64-bit keys, one row at a time
+        for (int rl = wave * RPW; rl < wave * RPW + RPW; ++rl) {
+            if (rl >= rows) break;
             const int p = p0 + rl;
             uint64_t key[E];
 #pragma unroll
@@ -243,29 +357,21 @@ __global__ __launch_bounds__(256) void score_rank_kernel(const float* __restrict
             }
             wave_bitonic_desc<E>(key, lane);
 #pragma unroll
-            for (int r = 0; r < E; ++r) s_keep[wave][lane * E + r] = 0;
+            for (int r = 0; r < E; ++r) s_keep[wave][0][lane * E + r] = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int r = 0; r < E; ++r)
-                if (lane * E + r < g.k) s_keep[wave][0xffffffffu - (uint32_t)key[r]] = 1;
+                if (lane * E + r < g.k) s_keep[wave][0][0xffffffffu - (uint32_t)key[r]] = 1;
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
-
-            const int32_t i = cand_block(g, p);
-            const uint8_t* kp_row = s_keep[wave];
-            const int32_t w = g.w;
-            compact_row(g, lane, false, false, out.mask + (slice * nb + i) * nb,
-                        out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
-                        [&](int32_t j, int32_t code) {
-                            return kp_row[code] != 0 || (w >= 0 && abs(j - i) <= w);
-                        });
+            compact_sparse(p, s_keep[wave][0]);
             __builtin_amdgcn_wave_barrier();
         }
     }
 
     // ---- this workgroup's share of the PINNED and DROPPED rows
-    for (int t = tile * 4 + wave; t < g.n_other; t += n_tiles * 4) {
+    for (int t = tile * WAVES + wave; t < g.n_other; t += n_tiles * WAVES) {
         const int32_t i = other_block(g, t);
         const int32_t cls = block_class(g, i);
         compact_row(g, lane, cls == CLS_DROPPED, cls == CLS_PINNED,
@@ -318,9 +424,8 @@ static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int H
                                 const Geometry& g, float* qp, float* kp, hipStream_t s) {
     const int64_t items = (int64_t)B * (H + Hkv) * g.n_cand;
     const dim3 grid((unsigned)((items + 3) / 4));
-    if (block == 64) hipLaunchKernelGGL((pool_kernel<T, D, 64>), grid, dim3(256), 0, s, q, k, B, H, Hkv, g, qp, kp);
-    else hipLaunchKernelGGL((pool_kernel<T, D, 32>), grid, dim3(256), 0, s, q, k, B, H, Hkv, g, qp, kp);
-    return hipGetLastError();
+    if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp);
+    return launch(pool_kernel<T, D, 32>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp);
 }
 
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
@@ -338,11 +443,11 @@ hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int
 template <int D, int E>
 static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H, int Hkv,
                                  const Geometry& g, MaskOut out, hipStream_t s) {
-    constexpr int RT = (E <= 8) ? 32 : 16;
+    constexpr int RT = RankShape<E>::RT;
     const int n_tiles = (g.n_cand + RT - 1) / RT;
     const dim3 grid((unsigned)((int64_t)B * H * n_tiles));
-    hipLaunchKernelGGL((score_rank_kernel<D, E>), grid, dim3(256), 0, s, qp, kp, B, H, Hkv, g, out, n_tiles);
-    return hipGetLastError();
+    return launch(score_rank_kernel<D, E>, grid, dim3(RankShape<E>::WAVES * 64), s, qp, kp, B, H, Hkv, g,
+                  out, n_tiles);
 }
 
 template <int D>
@@ -366,8 +471,7 @@ hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int
 
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s) {
     const dim3 grid((unsigned)((g.nb + 3) / 4), (unsigned)slices);
-    hipLaunchKernelGGL(layout_kernel, grid, dim3(256), 0, s, g, out);
-    return hipGetLastError();
+    return launch(layout_kernel, grid, dim3(256), s, g, out);
 }
 
 }  // namespace bsattn

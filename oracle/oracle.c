@@ -44,7 +44,12 @@
  *
  * Parity pins: every function here is checked by the CPU tests against
  * brute force, closed forms, library routines (float64 sdpa) or values
- * printed in the pages; none is "parity unpinned".
+ * printed in the pages.  One reading stays partly unpinned: how a fractional
+ * budget rounds to k (floor here).  The pages print no k for any layout, so
+ * beyond the cases where every rounding agrees (8 candidates at 0.5, budget
+ * 1.0) the floor is "parity unpinned"; the GPU library follows the same
+ * reading, and the tests pin its properties (never above the budget, at
+ * least 1, full budget reports dense).
  */
 #include <math.h>
 #include <stdint.h>

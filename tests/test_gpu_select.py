@@ -147,3 +147,58 @@ def test_radial_video_workload_matches_selector_density(cuda):
     sc = sel.count.cpu().numpy()
     assert np.array_equal(np.broadcast_to(c, sc.shape), sc)
     assert set(np.unique(c).tolist()) == {0, 155, 514}
+
+
+def boundary_case(n, D, k, seed, negative=False):
+    """fp32 Q/K whose block-mean scores put every row's last-kept / first-dropped
+    pair just outside the 1e-4 near-tie window (1.0001e-4 .. 1.2e-4 relative),
+    at magnitudes just below and just above powers of two.
+
+    Q block i = (1 + i // D) * e_(i % D) on every token; K block j = column
+    v[:, j] on every token, so score(i, j) = (1 + i // D) * v[i % D, j]
+    exactly.  Rows of one pattern d = i % D share v[d, :]; the D-periodic
+    diagonal positions get the smallest values so removing the diagonal never
+    moves the boundary.
+    """
+    rng = np.random.default_rng(seed)
+    v = np.zeros((D, n))
+    for d in range(D):
+        diag_like = [j for j in range(n) if j % D == d]
+        others = [j for j in range(n) if j % D != d]
+        order = rng.permutation(others)
+        x = float(2.0 ** rng.integers(-3, 4)) * (1 - 2.0 ** -12 if rng.random() < 0.5 else 1 + 2.0 ** -12)
+        delta = rng.uniform(1.0001e-4, 1.2e-4)
+        vals = np.empty(len(order))
+        top = k - 1                                  # non-diagonal kept per row
+        vals[top - 1] = x * (1 + delta)              # last kept
+        vals[top] = x                                # first dropped
+        for r in range(top - 2, -1, -1):
+            vals[r] = vals[r + 1] * (1 + rng.uniform(2e-3, 1e-2))
+        for r in range(top + 1, len(order)):
+            vals[r] = vals[r - 1] * (1 - rng.uniform(2e-3, 1e-2))
+        if negative:
+            vals = -vals[::-1]
+            vals_ordered = np.empty_like(vals)
+            vals_ordered[:] = vals
+            # negate and reverse keeps the boundary gap; ranks flip accordingly
+        v[d, order] = np.float32(vals)
+        v[d, diag_like] = np.float32(np.min(vals) - 1.0) if not negative else np.float32(np.min(vals) * 1.5)
+    block = 64
+    N = n * block
+    q = np.zeros((1, 1, N, D), np.float32)
+    kk = np.zeros((1, 1, N, D), np.float32)
+    for i in range(n):
+        q[0, 0, i * block:(i + 1) * block, i % D] = 1 + i // D
+        kk[0, 0, i * block:(i + 1) * block, :] = v[:, i]
+    return torch.from_numpy(q), torch.from_numpy(kk)
+
+
+@pytest.mark.parametrize("n,D,negative", [(64, 64, False), (64, 64, True), (512, 128, False), (512, 128, True)])
+def test_select_rank_resolution_outside_tie_window(cuda, n, D, negative):
+    budget = 0.3
+    k = oracle.budget(n, budget)[0]
+    q, kk = boundary_case(n, D, k, seed=n + D + int(negative), negative=negative)
+    bm = run_select(q.to(cuda), kk.to(cuda), (), 64, budget)
+    ref, tie = oracle_select(q, kk, (), 64, budget)
+    assert tie.sum() == 0, "the construction must keep every row outside the near-tie window"
+    assert compare_masks(bm, ref, tie) == 0

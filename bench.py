@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every step from the host instead of replaying a captured HIP graph")
     return p.parse_args()
 
 
@@ -150,11 +152,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # whole-step throughput: K steps (select + forward), host clock, synchronised on both sides
-    torch.cuda.synchronize()
+    # One step = select + forward.  By default the step is captured once as a
+    # HIP graph and replayed, so the host's per-call launch cost stays out of
+    # the GPU timeline; --eager launches every call from the host.
+    run_step = step
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=cap)
+                hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+    # whole-step throughput: K steps, host clock, synchronised on both sides
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -213,6 +233,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded; clustered Q/K for image workloads)",
+        "step_launch": "eager" if args.eager else "hip graph replay",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
                    "block": w.block, "budget": w.budget, "k": bm.k, "layer": args.layer,
                    "segments": [list(s) for s in w.segments], "window_tokens": w.window_tokens,

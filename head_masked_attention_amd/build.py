@@ -18,6 +18,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libbsattn.so")
 SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip"]
 HEADERS = ["common.h", "internal.h"]
+# Per-source extra flags.  The attention kernel's scores come out of MFMA
+# accumulators and are never NaN for finite inputs; without NaN semantics
+# fmaxf lowers to bare v_max / v_max3 instead of also quieting each input
+# first.  (NaN in Q, K or V gives unspecified output.)
+EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -49,7 +54,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

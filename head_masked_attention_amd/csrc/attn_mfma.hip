@@ -1,10 +1,12 @@
 // Block-sparse attention forward, bf16 MFMA path (gfx950).
 //
-// One workgroup of two wavefronts per (b, h, 64-token query block); each
-// wavefront owns 32 query rows.  The workgroup walks the compacted list of
-// kept key blocks (CSR-like, ascending) in stages of KT keys:
+// One workgroup per (b, h, 64-token query block).  A pair of wavefronts
+// covers the 64 query rows (32 each); with SPLIT = 2 a second pair takes every
+// other kept key block and the two partial softmax states are merged at the
+// end.  Each pair walks its share of the compacted list of kept key blocks
+// (CSR-like, ascending) in stages of KT keys:
 //   - K and V stage tiles go from HBM/L2 straight into LDS with
-//     global_load_lds_dwordx4 (no register staging), NST stages deep, one
+//     global_load_lds_dwordx4 (no register staging), two stages deep, one
 //     barrier per stage;
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the Q^T fragments held in
 //     VGPRs for the whole loop;
@@ -65,6 +67,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
+__device__ __forceinline__ int g16_of(int lane) { return lane >> 4; }
+
+// max / sum of x over the lane pair (l, l ^ 32).  v_permlane32_swap (gfx950)
+// exchanges the two 32-lane halves in the VALU, without the LDS crossbar
+// round trip of ds_bpermute: of the pair it returns, one element is x and the
+// other the partner's x, in either order.
+__device__ __forceinline__ float pair_max32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -72,33 +89,38 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// ROWSUM_MFMA: the softmax denominators come from one extra O^T tile whose
-// A operand is all ones (the MFMA pipe sums the bf16 P it multiplies);
-// otherwise the VALU sums packed P with bf16 dot products.
-template <int D, int KT, int NST, bool ROWSUM_MFMA, int WPE>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
+// SPLIT key-block groups per workgroup: group g (wavefronts 2g, 2g + 1)
+// takes the kept blocks at list positions g, g + SPLIT, g + 2 SPLIT, ...
+// with its own LDS stages, and the groups' partial softmax states are merged
+// through LDS at the end.  More wavefronts per query block hide more latency
+// when the grid alone cannot fill the chip.
+template <int D, int KT, int SPLIT, int WPE, bool HOIST, bool LAUNDER, bool VSINGLE>
+__global__ __launch_bounds__(128 * SPLIT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int NI = KT * CPR / 128;       // loads per thread per tensor per stage
-    constexpr int TILE_ELEMS = KT * D;       // bf16 elements per K (or V) stage tile
+    constexpr int TILE = KT * D;             // bf16 elements per K (or V) stage tile
     constexpr int NKT = KT / 32;             // 32-key S^T tiles per stage
     constexpr int NKS = D / 16;              // k-steps of S^T
     constexpr int NDT = D / 32;              // 32-row d tiles of O^T
     constexpr int NPS = KT / 16;             // 16-key steps of O^T per stage
     constexpr int SUB = BLK / KT;            // stages per key block
+    constexpr int NT = 128 * SPLIT;          // threads per workgroup
     constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
     static_assert(NI >= 1 && KT * CPR % 128 == 0, "stage tiling");
+    static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
+    static_assert(SPLIT == 1 || SPLIT * TILE * 2 >= D * 128, "merge buffer fits in one stage object");
+    static_assert(!(VSINGLE && HOIST), "a single V stage is read only after its own barrier");
 
-    // one LDS object per stage: distinct objects let the compiler see that the
-    // reads of one stage never alias the loads in flight into the others
-    __shared__ __attribute__((aligned(16))) uint16_t K0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t V0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t K1[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t V1[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t K2[NST > 2 ? TILE_ELEMS : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t V2[NST > 2 ? TILE_ELEMS : 8];
-    static_assert(NST == 2 || NST == 3, "two or three LDS stages");
+    // one LDS object per stage (holding every group's tile): distinct objects
+    // let the compiler see that the reads of one stage never alias the loads
+    // in flight into the other
+    __shared__ __attribute__((aligned(16))) uint16_t K0[SPLIT * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t V0[SPLIT * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t K1[SPLIT * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t V1[VSINGLE ? 8 : SPLIT * TILE];
+    static_assert((TILE * 2) % (D * 2) == 0, "tiles hold whole rows");
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
@@ -110,6 +132,9 @@ void attn_mfma_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 1;               // key-block group
+    const int wq = wave & 1;                 // query rows 32*wq .. 32*wq + 31
+    const int gtid = tid & 127;              // thread within the group
     const int hl = lane >> 5, ql = lane & 31;
 
     const bool active = (a.head_mask == nullptr) || (a.head_mask[h] != 0);
@@ -124,7 +149,7 @@ void attn_mfma_kernel(AttnArgs a) {
 
     if (!active || cnt <= 0) {
         const uint4 z = {0u, 0u, 0u, 0u};
-        for (int c = tid; c < BLK * CPR; c += 128)
+        for (int c = tid; c < BLK * CPR; c += NT)
             *(uint4*)(obase + (int64_t)(c / CPR) * a.o_sn + (c % CPR) * 8) = z;
         return;
     }
@@ -133,75 +158,144 @@ void attn_mfma_kernel(AttnArgs a) {
     const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.sb + kvh * a.k.sh;
     const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sb + kvh * a.v.sh;
 
-    // Q^T fragments: lane holds Q[32*wave + ql][16*ks + 8*hl + 0..7]
+    // Q^T fragments: lane holds Q[32*wq + ql][16*ks + 8*hl + 0..7]
     bf16x8 qf[NKS];
     {
-        const uint16_t* qr = qbase + (int64_t)(32 * wave + ql) * a.q.sn + 8 * hl;
+        const uint16_t* qr = qbase + (int64_t)(32 * wq + ql) * a.q.sn + 8 * hl;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
     }
-    const int T = cnt * SUB;   // stages
+    // every group runs the same number of stages (the barriers are
+    // workgroup-wide); stages past the group's own blocks only synchronise
+    const int T = ((cnt + SPLIT - 1) / SPLIT) * SUB;
+    const int Tg = ((cnt - grp + SPLIT - 1) / SPLIT) * SUB;
     // kept key block of stage t: a scalar (constant address space) load, so
     // waiting for it never waits for the stage loads in flight
     const __attribute__((address_space(4))) int32_t* klist =
         (const __attribute__((address_space(4))) int32_t*)list;
     auto block_of = [&](int t) -> int32_t {
-        const int i = t / SUB;
+        const int i = (t / SUB) * SPLIT + grp;
         return list == nullptr ? i : klist[i];
     };
-    // per-thread source offsets of the NI chunks it loads per stage: LDS chunk
-    // slot s = i*128 + tid holds row s / CPR, global chunk (s % CPR) ^ swizzle
+    // per-thread source offsets of the NI chunks it loads per stage: chunk
+    // slot s = i*128 + gtid of the group's tile holds row s / CPR, global
+    // chunk (s % CPR) ^ swizzle
     int32_t koff[NI], voff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int s = i * 128 + tid;
+        const int s = i * 128 + gtid;
         const int r = s / CPR;
         const int c = (s % CPR) ^ chunk_swizzle<D>(r);
         koff[i] = r * (int32_t)a.k.sn + c * 8;
         voff[i] = r * (int32_t)a.v.sn + c * 8;
     }
-    // issue the K and V loads of stage t into LDS buffer (Kd, Vd)
-    auto issue = [&](int t, uint16_t* Kd, uint16_t* Vd) {
+    // issue the K (or V) loads of stage t into the group's tile at Kd (Vd)
+    auto issue_k = [&](int t, uint16_t* Kd) {
         const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
         const uint16_t* kt = kbase + row0 * a.k.sn;
-        const uint16_t* vt = vbase + row0 * a.v.sn;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int dst = (i * 128 + wave * 64) * 8;   // wave-uniform element offset
+        for (int i = 0; i < NI; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(kt + koff[i]),
-                (__attribute__((address_space(3))) void*)(Kd + dst), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(Kd + (i * 128 + wq * 64) * 8), 16, 0, 0);
+    };
+    auto issue_v = [&](int t, uint16_t* Vd) {
+        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+        const uint16_t* vt = vbase + row0 * a.v.sn;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(vt + voff[i]),
-                (__attribute__((address_space(3))) void*)(Vd + dst), 16, 0, 0);
-        }
+                (__attribute__((address_space(3))) void*)(Vd + (i * 128 + wq * 64) * 8), 16, 0, 0);
     };
-    issue(0, K0, V0);
-    if (NST > 2 && T > 1) issue(1, K1, V1);
+    // With VSINGLE the group has one V tile: V of stage t is loaded after the
+    // stage's first barrier (every wave is past the previous P V) and waited
+    // for at a second barrier before this stage's P V, while K stays double
+    // buffered.  This keeps the workgroup's LDS small enough for five
+    // workgroups per CU.
+    if (Tg > 0) {
+        issue_k(0, K0 + grp * TILE);
+        if constexpr (!VSINGLE) issue_v(0, V0 + grp * TILE);
+    }
+
+    // Per-lane byte offsets of this lane's LDS fragments within a stage
+    // object (the group's tile included).  Row bases are multiples of the row
+    // size and the swizzle acts on the 16-byte chunk field only, so a
+    // fragment further along the contraction (ks) or along d (dt) is the
+    // base XOR a constant, and a later 16-key step is the base plus a
+    // constant: three registers instead of one address per fragment.
+    //   K fragment ks:  kb ^ (32 ks)          (chunk (2ks + hl) ^ swz(r))
+    //   V operand (dt, ks): (vb0 ^ (64 dt)) + 32 D ks, and vb1 for rows + 4
+    uint32_t kb, vb0, vb1;
+    {
+        const int r = slot_key(ql);
+        kb = (uint32_t)(grp * TILE * 2 + r * D * 2 + 16 * (hl ^ chunk_swizzle<D>(r)));
+        const int c0 = 2 * (g16_of(lane) & 1) + ((lane & 3) >> 1);
+        const int half = lane & 1;
+        const int r0 = 8 * hl + ((lane & 15) >> 2), r1 = r0 + 4;
+        vb0 = (uint32_t)(grp * TILE * 2 + r0 * D * 2 + 16 * (c0 ^ chunk_swizzle<D>(r0)) + 8 * half);
+        vb1 = (uint32_t)(grp * TILE * 2 + r1 * D * 2 + 16 * (c0 ^ chunk_swizzle<D>(r1)) + 8 * half);
+    }
 
     const float sl2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
     float m_run = -INFINITY, l_run = 0.f;
     f16v oacc[NDT];
-    f16v lacc;                                          // row sums (ROWSUM_MFMA)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
-    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-    const int g16 = lane >> 4, j16 = lane & 15;
-
-    // one stage: wait for its tiles (the next stage's loads may stay in
-    // flight), make them visible, start the loads of stage t + NST - 1 into
-    // the buffers freed by stage t - 1, then compute from this stage
+    // one stage: wait for its tiles, make them visible, start the loads of
+    // stage t + 1 into the buffers freed by stage t - 1, then compute
     auto stage = [&](int t, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
-        if (NST > 2 && t + 1 < T) wait_vmcnt<(NST > 2 ? 2 * NI : 0)>();
-        else wait_vmcnt<0>();
+        wait_vmcnt<0>();
         __syncthreads();
-        if (t + NST - 1 < T) issue(t + NST - 1, Kn, Vn);
+        if constexpr (VSINGLE) {
+            if (t < Tg) issue_v(t, V0 + grp * TILE);
+            if (t + 1 < Tg) issue_k(t + 1, Kn);
+        } else if (t + 1 < Tg) {
+            issue_k(t + 1, Kn);
+            issue_v(t + 1, Vn);
+        }
+        if (t >= Tg) {
+            if constexpr (VSINGLE) __syncthreads();   // the stage's second barrier
+            return;
+        }
+
+        // with LAUNDER the offsets pass through an empty asm once per stage, so the
+        // compiler recomputes the XORs here instead of keeping every
+        // fragment address live across the loop
+        uint32_t kbs = kb, vbs0 = vb0, vbs1 = vb1;
+        if constexpr (LAUNDER) asm volatile("" : "+v"(kbs), "+v"(vbs0), "+v"(vbs1));
+        const uint8_t* Kb = (const uint8_t*)Kt;
+        const uint8_t* Vb = (const uint8_t*)Vt;
+
+        // V^T operands of O^T += V^T P^T.  Within each 16-lane group, lane j
+        // supplies V[kb + j/4][d0 + 4*(j%4) .. +3]; lane i then receives
+        // V[kb + 0..3][d0 + i].  With HOIST they are read, with the K
+        // fragments, at the top of the stage, so one LDS round trip covers both.
+        auto v_operand = [&](int dt, int ks) -> bf16x8 {
+            const uint32_t o0 = (vbs0 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
+            const uint32_t o1 = (vbs1 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
+            const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(Vb + o0));
+            const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(Vb + o1));
+            const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, both);
+        };
+        bf16x8 kf[NKT][NKS];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                kf[kt][ks] = *(const bf16x8*)(Kb + (kbs ^ (uint32_t)(32 * ks)) + 64 * D * kt);
+        bf16x8 vf[HOIST ? NDT : 1][HOIST ? NPS : 1];
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int ks = 0; ks < NPS; ++ks) vf[dt][ks] = v_operand(dt, ks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
         // S^T for NKT 32-key tiles
         f16v sacc[NKT];
@@ -209,28 +303,25 @@ void attn_mfma_kernel(AttnArgs a) {
         for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-            const int r = 32 * kt + slot_key(ql);
-            const int sw = chunk_swizzle<D>(r);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 kf = *(const bf16x8*)(Kt + (r * CPR + ((2 * ks + hl) ^ sw)) * 8);
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][ks], qf[ks], sacc[kt], 0, 0, 0);
         }
 
-        // online softmax with lazy rescaling; the row maximum as a tree
-        float mq[NKT * 4];
+        // online softmax with lazy rescaling; the row maximum as a tree of
+        // three-input maxima (v_max3_f32)
+        float mk[NKT];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt) {
+            const f16v& x = sacc[kt];
+            const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+            const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+            const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+            mk[kt] = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                mq[4 * kt + q] = fmaxf(fmaxf(sacc[kt][4 * q], sacc[kt][4 * q + 1]),
-                                       fmaxf(sacc[kt][4 * q + 2], sacc[kt][4 * q + 3]));
-#pragma unroll
-        for (int n = NKT * 4; n > 1; n >>= 1)
-#pragma unroll
-            for (int q = 0; q < n / 2; ++q) mq[q] = fmaxf(mq[q], mq[q + n / 2]);
-        float mx = fmaxf(mq[0], __shfl_xor(mq[0], 32)) * sl2;
+        for (int kt = 1; kt < NKT; ++kt) mk[0] = fmaxf(mk[0], mk[kt]);
+        const float mx = pair_max32(mk[0]) * sl2;
         const bool grow = mx > m_run + kTau;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
             const float m_new = grow ? mx : m_run;
@@ -241,12 +332,11 @@ void attn_mfma_kernel(AttnArgs a) {
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-            if constexpr (ROWSUM_MFMA)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
         }
 
-        bf16x8 pf[NPS];   // B operand of P V, one per 16-key step
+        // P in bf16, packed as the B operand of P V (one per 16-key step);
+        // row sums from bf16 dot products of the same packed values
+        bf16x8 pf[NPS];
         float psum2[2] = {0.f, 0.f};
         const bf2v one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
@@ -259,56 +349,67 @@ void attn_mfma_kernel(AttnArgs a) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_run));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_run));
                     w[e >> 1] = to_bf16x2(p0, p1);
-                    if constexpr (!ROWSUM_MFMA)
-                        psum2[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(w[e >> 1], one2, psum2[(e >> 1) & 1], false);
+                    psum2[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(w[e >> 1], one2, psum2[(e >> 1) & 1], false);
                 }
                 pf[2 * kt + u] = __builtin_bit_cast(
                     bf16x8, (uint4){__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
                                     __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3])});
-                if constexpr (ROWSUM_MFMA)
-                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[2 * kt + u], lacc, 0, 0, 0);
             }
         l_run += psum2[0] + psum2[1];
 
-        // O^T += V^T P^T.  Within each 16-lane group, lane j supplies
-        // V[kb + j/4][d0 + 4*(j%4) .. +3]; lane i then receives V[kb + 0..3][d0 + i].
+        if constexpr (VSINGLE) {
+            // this stage's V has landed; the next stage's K may still fly
+            if (t + 1 < Tg) wait_vmcnt<NI>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+        }
+
+        // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
-            const int c = d >> 3, half = (d >> 2) & 1;
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int ks = 0; ks < NPS; ++ks) {
-                const int r0 = 16 * ks + 8 * hl + (j16 >> 2);
-                const int r1 = r0 + 4;
-                const uint16_t* p0 = Vt + (r0 * CPR + (c ^ chunk_swizzle<D>(r0))) * 8 + half * 4;
-                const uint16_t* p1 = Vt + (r1 * CPR + (c ^ chunk_swizzle<D>(r1))) * 8 + half * 4;
-                const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p0));
-                const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p1));
-                const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[ks],
-                                                                  oacc[dt], 0, 0, 0);
+                const bf16x8 va = HOIST ? vf[HOIST ? dt : 0][HOIST ? ks : 0] : v_operand(dt, ks);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], oacc[dt], 0, 0, 0);
             }
-        }
     };
-    if constexpr (NST == 2) {
-        for (int t = 0; t < T; t += 2) {
-            stage(t, K0, V0, K1, V1);
-            if (t + 1 < T) stage(t + 1, K1, V1, K0, V0);
+    for (int t = 0; t < T; t += 2) {
+        stage(t, K0, V0, K1 + grp * TILE, (VSINGLE ? V0 : V1) + grp * TILE);
+        if (t + 1 < T) stage(t + 1, K1, VSINGLE ? V0 : V1, K0 + grp * TILE, V0 + grp * TILE);
+    }
+
+    if constexpr (SPLIT == 2) {
+        // merge: group 1 leaves its (O, m, l) in LDS, group 0 rescales both
+        // partial states to the larger running maximum and adds them.  No
+        // stage load is in flight here (the last stage waited for all).
+        __syncthreads();
+        float* po = (float*)(wq == 0 ? K0 : V0);        // [NDT * 16][64 lanes]
+        float* pml = (float*)K1 + wq * 128;              // m [64 lanes], l [64 lanes]
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) po[(dt * 16 + r) * 64 + lane] = oacc[dt][r];
+            pml[lane] = m_run;
+            pml[64 + lane] = l_run;
         }
-    } else {
-        // stage t reads buffer t % 3 and loads stage t + 2 into buffer (t + 2) % 3
-        for (int t = 0; t < T; t += 3) {
-            stage(t, K0, V0, K2, V2);
-            if (t + 1 < T) stage(t + 1, K1, V1, K0, V0);
-            if (t + 2 < T) stage(t + 2, K2, V2, K1, V1);
-        }
+        __syncthreads();
+        if (grp == 1) return;
+        // group 0 always has at least one block, so m_run is finite; a group 1
+        // without blocks has m = -inf and contributes exp2(-inf) = 0
+        const float m1 = pml[lane], l1 = pml[64 + lane];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a0 + po[(dt * 16 + r) * 64 + lane] * a1;
+        l_run = l_run * a0 + l1 * a1;
     }
 
     // normalise and store: oacc[dt][r] = O[query][32*dt + 8*(r/4) + 4*hl + r%4]
-    // every row of the ones tile holds the full sum of the bf16 P of this query
-    const float l_tot = ROWSUM_MFMA ? lacc[0] : l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = obase + (int64_t)(32 * wave + ql) * a.o_sn;
+    const float inv = 1.f / pair_sum32(l_run);
+    uint16_t* orow = obase + (int64_t)(32 * wq + ql) * a.o_sn;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -320,247 +421,53 @@ void attn_mfma_kernel(AttnArgs a) {
         }
 }
 
-// ---------------------------------------------------------------------------
-// Sixteen-row variant: four wavefronts per query block, each owning 16 query
-// rows, on v_mfma_f32_16x16x32_bf16.  Twice the wavefronts of the 32-row
-// kernel and a third of its registers, for shapes whose grids are too small to
-// hide latency with 32-row wavefronts.  Layouts (lane l, g = l / 16):
-//   S^T tile (16 keys x 16 queries): lane holds keys 4g..4g+3 of query l % 16;
-//   the PV step of 32 keys takes k-slots 8g + 4*kt + r = key 16*kt + 4g + r,
-//   so P never moves between lanes and each V^T operand is two transposing
-//   reads of four consecutive keys.
-// ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int chunk_swizzle16(int r) {
-    if constexpr (D == 64) return (r & 7) ^ ((r >> 1) & 7);
-    else return (r & 15) ^ ((r & 1) << 3);
-}
-
-typedef float f4v_ __attribute__((ext_vector_type(4)));
-
-template <int D, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
-void attn_m16_kernel(AttnArgs a) {
-    constexpr int BLK = 64, KT = 32;
-    constexpr int CPR = D / 8;
-    constexpr int NI = KT * CPR / 256;        // loads per thread per tensor per stage
-    constexpr int TILE_ELEMS = KT * D;
-    constexpr int NKS = D / 32;               // k-steps of S^T
-    constexpr int NDT = D / 16;               // 16-row d tiles of O^T
-    constexpr int SUB = BLK / KT;
-    constexpr float kTau = 8.0f;
-    static_assert(NI >= 1 && KT * CPR % 256 == 0, "stage tiling");
-
-    __shared__ __attribute__((aligned(16))) uint16_t K0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t V0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t K1[TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t V1[TILE_ELEMS];
-
-    const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (L >= a.n_work) return;
-    const int32_t qb = (int32_t)(L % a.nqb);
-    const int64_t bh = L / a.nqb;
-    const int32_t h = (int32_t)(bh % a.H);
-    const int32_t b = (int32_t)(bh / a.H);
-    const int32_t kvh = h / (a.H / a.Hkv);
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, li = lane & 15;
-
-    const bool active = (a.head_mask == nullptr) || (a.head_mask[h] != 0);
-    int32_t cnt = a.nkb;
-    const int32_t* list = nullptr;
-    if (a.count != nullptr) {
-        const int64_t ms = (int64_t)(a.mB == 1 ? 0 : b) * a.mH + (a.mH == 1 ? 0 : h);
-        cnt = a.count[ms * a.nqb + qb];
-        list = a.index + (ms * a.nqb + qb) * (int64_t)a.nkb;
-    }
-    uint16_t* obase = (uint16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qb * BLK * a.o_sn;
-    if (!active || cnt <= 0) {
-        const uint4 z = {0u, 0u, 0u, 0u};
-        for (int c = tid; c < BLK * CPR; c += 256)
-            *(uint4*)(obase + (int64_t)(c / CPR) * a.o_sn + (c % CPR) * 8) = z;
-        return;
-    }
-    const uint16_t* qbase = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qb * BLK * a.q.sn;
-    const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.sb + kvh * a.k.sh;
-    const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sb + kvh * a.v.sh;
-
-    // Q^T fragments: lane holds Q[16*wave + li][32*ks + 8*g + 0..7]
-    bf16x8 qf[NKS];
-    {
-        const uint16_t* qr = qbase + (int64_t)(16 * wave + li) * a.q.sn + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qr + 32 * ks);
-    }
-    int32_t koff[NI], voff[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int s = i * 256 + tid;
-        const int r = s / CPR;
-        const int c = (s % CPR) ^ chunk_swizzle16<D>(r);
-        koff[i] = r * (int32_t)a.k.sn + c * 8;
-        voff[i] = r * (int32_t)a.v.sn + c * 8;
-    }
-    const int T = cnt * SUB;
-    const __attribute__((address_space(4))) int32_t* klist =
-        (const __attribute__((address_space(4))) int32_t*)list;
-    auto issue = [&](int t, uint16_t* Kd, uint16_t* Vd) {
-        const int i0 = t / SUB;
-        const int32_t blk = list == nullptr ? i0 : klist[i0];
-        const int64_t row0 = (int64_t)blk * BLK + (t % SUB) * KT;
-        const uint16_t* kt = kbase + row0 * a.k.sn;
-        const uint16_t* vt = vbase + row0 * a.v.sn;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int dst = (i * 256 + wave * 64) * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + koff[i]),
-                                             (__attribute__((address_space(3))) void*)(Kd + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + voff[i]),
-                                             (__attribute__((address_space(3))) void*)(Vd + dst), 16, 0, 0);
-        }
-    };
-    issue(0, K0, V0);
-
-    const float sl2 = a.scale * 1.4426950408889634f;
-    float m_run = -INFINITY, l_run = 0.f;
-    f4v_ oacc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = (f4v_){0.f, 0.f, 0.f, 0.f};
-    const bf2v one2 = {(__bf16)1.f, (__bf16)1.f};
-
-    auto stage = [&](int t, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (t + 1 < T) issue(t + 1, Kn, Vn);
-
-        // S^T: two 16-key tiles
-        f4v_ sacc[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = (f4v_){0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * kt + li;
-            const int sw = chunk_swizzle16<D>(r);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 kf = *(const bf16x8*)(Kt + (r * CPR + ((4 * ks + g) ^ sw)) * 8);
-                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
-            }
-        }
-        // row max over the 32 keys: 8 in lane, then the four lane groups
-        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        const bool grow = mx > m_run + kTau;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-        }
-        // P: k-slot 8g + 4kt + r <-> key 16kt + 4g + r
-        bf2v w[4];
-        float psum2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_run));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r + 1], sl2, -m_run));
-                w[2 * kt + r / 2] = to_bf16x2(p0, p1);
-                psum2[kt] = __builtin_amdgcn_fdot2_f32_bf16(w[2 * kt + r / 2], one2, psum2[kt], false);
-            }
-        l_run += psum2[0] + psum2[1];
-        const bf16x8 pf = __builtin_bit_cast(
-            bf16x8, (uint4){__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
-                            __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3])});
-        // O^T += V^T P^T: per 16-lane group, lane j supplies V[kb + j/4][16*dt + 4*(j%4)]
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int d = 16 * dt + 4 * (li & 3);
-            const int c = d >> 3, half = (d >> 2) & 1;
-            const int r0 = 4 * g + (li >> 2);
-            const int r1 = r0 + 16;
-            const uint16_t* p0 = Vt + (r0 * CPR + (c ^ chunk_swizzle16<D>(r0))) * 8 + half * 4;
-            const uint16_t* p1 = Vt + (r1 * CPR + (c ^ chunk_swizzle16<D>(r1))) * 8 + half * 4;
-            const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p0));
-            const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p1));
-            const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, oacc[dt], 0, 0, 0);
-        }
-    };
-    for (int t = 0; t < T; t += 2) {
-        stage(t, K0, V0, K1, V1);
-        if (t + 1 < T) stage(t + 1, K1, V1, K0, V0);
-    }
-
-    // l over the row: the four lane groups hold disjoint keys
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const float inv = 1.f / l_tot;
-    // oacc[dt][r] = O[query 16*wave + li][16*dt + 4g + r]
-    uint16_t* orow = obase + (int64_t)(16 * wave + li) * a.o_sn;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        uint2 w2;
-        w2.x = pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv);
-        w2.y = pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv);
-        *(uint2*)(orow + 16 * dt + 4 * g) = w2;
-    }
-}
-
-// Launch shapes (keys per LDS stage, row-sum mode, waves per EU) per head dim.
+// Launch shapes per head dim: keys per LDS stage, key-block groups per
+// workgroup, waves per EU, hoisted V reads.  Chosen by measured sweeps.
 #ifndef BSATTN_D64_KT
 #define BSATTN_D64_KT 32
 #endif
-#ifndef BSATTN_D64_ROWSUM_MFMA
-#define BSATTN_D64_ROWSUM_MFMA false
+#ifndef BSATTN_D64_SPLIT
+#define BSATTN_D64_SPLIT 2
 #endif
 #ifndef BSATTN_D64_WPE
-#define BSATTN_D64_WPE 3
+#define BSATTN_D64_WPE 5
+#endif
+#ifndef BSATTN_D64_HOIST
+#define BSATTN_D64_HOIST false
+#endif
+#ifndef BSATTN_D64_LAUNDER
+#define BSATTN_D64_LAUNDER false
+#endif
+#ifndef BSATTN_D128_LAUNDER
+#define BSATTN_D128_LAUNDER false
+#endif
+#ifndef BSATTN_D64_VSINGLE
+#define BSATTN_D64_VSINGLE true
+#endif
+#ifndef BSATTN_D128_VSINGLE
+#define BSATTN_D128_VSINGLE false
 #endif
 #ifndef BSATTN_D128_KT
 #define BSATTN_D128_KT 32
 #endif
-#ifndef BSATTN_D128_ROWSUM_MFMA
-#define BSATTN_D128_ROWSUM_MFMA false
+#ifndef BSATTN_D128_SPLIT
+#define BSATTN_D128_SPLIT 1
 #endif
 #ifndef BSATTN_D128_WPE
 #define BSATTN_D128_WPE 2
 #endif
-#ifndef BSATTN_D64_NST
-#define BSATTN_D64_NST 2
-#endif
-#ifndef BSATTN_D128_NST
-#define BSATTN_D128_NST 2
-#endif
-// 16-row kernel per head dim (0 = the 32-row kernel) and its waves per EU
-#ifndef BSATTN_D64_ROWS16
-#define BSATTN_D64_ROWS16 0
-#endif
-#ifndef BSATTN_D128_ROWS16
-#define BSATTN_D128_ROWS16 0
-#endif
-#ifndef BSATTN_M16_WPE
-#define BSATTN_M16_WPE 4
+#ifndef BSATTN_D128_HOIST
+#define BSATTN_D128_HOIST true
 #endif
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {
     const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
     const dim3 grid((unsigned)padded);
-    if (D == 128 && BSATTN_D128_ROWS16)
-        return launch(attn_m16_kernel<128, BSATTN_M16_WPE>, grid, dim3(256), s, a);
-    if (D == 64 && BSATTN_D64_ROWS16)
-        return launch(attn_m16_kernel<64, BSATTN_M16_WPE>, grid, dim3(256), s, a);
     if (D == 128)
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_NST, BSATTN_D128_ROWSUM_MFMA, BSATTN_D128_WPE>, grid,
-                      dim3(128), s, a);
-    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_NST, BSATTN_D64_ROWSUM_MFMA, BSATTN_D64_WPE>, grid, dim3(128),
-                  s, a);
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, BSATTN_D128_WPE, BSATTN_D128_HOIST, BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE>,
+                      grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, BSATTN_D64_WPE, BSATTN_D64_HOIST, BSATTN_D64_LAUNDER, BSATTN_D64_VSINGLE>,
+                  grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }
 
 }  // namespace bsattn

@@ -185,8 +185,8 @@ bsattn_status bsattn_budget_k(int32_t n_cand, double budget, int32_t* k, int32_t
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int32_t block,
                                      int64_t D) {
     if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || (block != 32 && block != 64)) return 0;
-    const size_t nb = (size_t)(N / block);
-    return align256((size_t)B * H * nb * D * 4) + align256((size_t)B * Hkv * nb * D * 4);
+    const size_t rows = (size_t)pooled_rows(N / block);   // >= pooled rows of any layout
+    return align256((size_t)B * H * rows * D * 4) + align256((size_t)B * Hkv * rows * D * 4);
 }
 
 bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
@@ -223,7 +223,7 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
         e = launch_layout_fill(g, (int)(q->B * q->H), mo, s);
     } else {
         float* qp = (float*)workspace;
-        float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * nb * q->D * 4));
+        float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
         e = launch_pool(q->dtype == BSATTN_F32, (int)q->D, layout->block, view_of(q), view_of(k),
                         (int)q->B, (int)q->H, (int)k->H, g, qp, kp, s);
         if (e == hipSuccess)

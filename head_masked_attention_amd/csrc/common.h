@@ -21,6 +21,10 @@ constexpr int kMaxRuns = 72;      // class runs; <= 2 * BSATTN_MAX_SEGMENTS + 1 
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int kMaxCand = 2048;    // sparsifiable blocks handled by the selector
 
+// Rows per (b, head) of the pooled sums in the selector workspace: the
+// candidates, padded to whole 16-row tiles.
+__host__ __device__ __forceinline__ int64_t pooled_rows(int64_t n_cand) { return (n_cand + 15) / 16 * 16; }
+
 // Per-layout geometry, host-computed once per call and passed by value.
 struct Geometry {
     int32_t nb;          // blocks in the sequence (N / block)

@@ -23,6 +23,23 @@ namespace bsattn {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
+// Pooled sums in the workspace, per (b, head): row tiles of 16 candidates,
+// each laid out in the order the score MFMA (16x16x4 fp32) reads them.  With
+// KQ = D / 4, lane l = li + 16 gq of the MFMA takes row li of the tile and d
+// = gq KQ + 4 c + e for k-step (c, e); element (row p, d) sits at
+//   tile(p) * 16 D + ((c * 4 + gq) * 16 + li) * 4 + e
+// so each lane's four k-steps of one c are one 16-byte read, and the 64
+// lanes of a wavefront read 1 KB of consecutive bytes per c.  Rows are padded
+// to a multiple of 16 per head.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int64_t pooled_offset(int32_t p, int32_t d) {
+    constexpr int KQ = D / 4;
+    const int li = p & 15, gq = d / KQ, c = (d % KQ) >> 2, e = d & 3;
+    return (int64_t)(p >> 4) * 16 * D + ((c * 4 + gq) * 16 + li) * 4 + e;
+}
+
+// ---------------------------------------------------------------------------
 // K1: block sums.  One wavefront per (tensor, b, head, candidate block).
 // Ranking by <sum Q_i, sum K_j> equals ranking by the mean-pooled score: the
 // factor 1/block^2 is a positive constant.
@@ -45,13 +62,14 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
 
     const TView* src;
     int64_t rem, heads;
-    float* dst;
-    if (item < nq) { src = &q; rem = item; heads = H; dst = qp + item * D; }
-    else { src = &k; rem = item - nq; heads = Hkv; dst = kp + rem * D; }
+    float* out;
+    if (item < nq) { src = &q; rem = item; heads = H; out = qp; }
+    else { src = &k; rem = item - nq; heads = Hkv; out = kp; }
     const int64_t p = rem % g.n_cand;
     const int64_t hh = (rem / g.n_cand) % heads;
     const int64_t b = rem / (g.n_cand * heads);
     const int64_t blk = cand_block(g, (int32_t)p);
+    float* dst = out + (b * heads + hh) * (int64_t)pooled_rows(g.n_cand) * D;
 
     const T* base = (const T*)src->p + b * src->sb + hh * src->sh +
                     (blk * BLOCK + lane / CPR) * src->sn + (lane % CPR) * EPC;
@@ -84,9 +102,10 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
         for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
 
     if (lane < CPR) {
-        float* o = dst + lane * EPC;
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4) *(f4v*)(o + e) = f4v{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        for (int e = 0; e < EPC; e += 4)
+            *(f4v*)(dst + pooled_offset<D>((int32_t)p, lane * EPC + e)) =
+                f4v{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
     }
 }
 
@@ -140,30 +159,64 @@ __device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[E], int lane) 
     }
 }
 
-// Writes one mask row (all nkb columns), its ascending index list and count,
+// Column codes of a whole row, cached in LDS by the kernels below when the
+// sequence has at most kCodeTable blocks (else column_code scans the runs).
+constexpr int kCodeTable = 1024;
+
+// Writes one mask row (all nb columns), its ascending index list and count,
 // with one wavefront.  keep(j, code) decides SPARSE columns; PINNED columns
 // are kept and DROPPED ones are not, unless `row_dropped` (then nothing).
+// Each lane takes four consecutive columns per pass: the mask goes out as one
+// 32-bit store per lane (vec4: nb % 4 == 0 and a 4-byte aligned mask), and a
+// lane's slot in the index list is the wavefront prefix sum of the per-lane
+// counts (0..4), taken bit-plane by bit-plane with ballots.
 template <typename KeepFn>
-__device__ __forceinline__ void compact_row(const Geometry& g, int lane, bool row_dropped,
-                                            bool row_pinned, uint8_t* mrow, int32_t* irow,
-                                            int32_t* cnt_out, KeepFn keep) {
+__device__ __forceinline__ void compact_row(const Geometry& g, const int16_t* codes, bool vec4, int lane,
+                                            bool row_dropped, bool row_pinned, uint8_t* mrow,
+                                            int32_t* irow, int32_t* cnt_out, KeepFn keep) {
+    const uint64_t below = (1ull << lane) - 1ull;
     int32_t cnt = 0;
-    for (int32_t j0 = 0; j0 < g.nb; j0 += 64) {
-        const int32_t j = j0 + lane;
-        bool v = false;
-        if (j < g.nb && !row_dropped) {
-            const int32_t code = column_code(g, j);
-            if (code == -2) v = false;
-            else if (code == -1 || row_pinned) v = true;
-            else v = keep(j, code);
+    for (int32_t j0 = 0; j0 < g.nb; j0 += 256) {
+        const int32_t jl = j0 + 4 * lane;
+        uint32_t bits = 0;
+        int c = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int32_t j = jl + u;
+            bool v = false;
+            if (j < g.nb && !row_dropped) {
+                const int32_t code = codes != nullptr ? (int32_t)codes[j] : column_code(g, j);
+                if (code == -2) v = false;
+                else if (code == -1 || row_pinned) v = true;
+                else v = keep(j, code);
+            }
+            bits |= (uint32_t)v << (8 * u);
+            c += v ? 1 : 0;
         }
-        const uint64_t bal = __ballot(v);
-        const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-        if (v) irow[cnt + before] = j;
-        if (j < g.nb) mrow[j] = v ? 1 : 0;
-        cnt += __popcll(bal);
+        const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
+        int32_t n = cnt + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if ((bits >> (8 * u)) & 1u) irow[n++] = jl + u;
+        if (vec4) {
+            if (jl < g.nb) *(uint32_t*)(mrow + jl) = bits;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (jl + u < g.nb) mrow[jl + u] = (uint8_t)((bits >> (8 * u)) & 1u);
+        }
+        cnt += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
     }
     if (lane == 0) *cnt_out = cnt;
+}
+
+// Fills the LDS column-code table (all threads of the workgroup take part;
+// the caller synchronises before use).  Returns the table, or nullptr when
+// the sequence is too long for it.
+__device__ __forceinline__ const int16_t* fill_codes(const Geometry& g, int16_t* table) {
+    if (g.nb > kCodeTable) return nullptr;
+    for (int32_t j = threadIdx.x; j < g.nb; j += blockDim.x) table[j] = (int16_t)column_code(g, j);
+    return table;
 }
 
 // Descending bitonic sort of R independent rows of 64*E 32-bit keys, one
@@ -208,7 +261,7 @@ __device__ __forceinline__ void wave_bitonic_desc32(uint32_t (&key)[R][E], int l
 template <int E>
 struct RankShape {
     static constexpr int RT = (E <= 2) ? 16 : (E <= 8 ? 32 : 16);
-    static constexpr int WAVES = (E <= 2) ? 4 : 8;
+    static constexpr int WAVES = 8;
 };
 
 // ---------------------------------------------------------------------------
@@ -238,6 +291,9 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     static_assert(RPW >= 1 && (!K32 || RPW % 2 == 0), "rows per wavefront");
     __shared__ float s_score[RT * SSTR];
     __shared__ uint8_t s_keep[WAVES][K32 ? 2 : 1][NPAD];
+    __shared__ int16_t s_code[kCodeTable];
+    const int16_t* codes = fill_codes(g, s_code);
+    const bool vec4 = (g.nb & 3) == 0 && ((uintptr_t)out.mask & 3u) == 0;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tile = blockIdx.x % n_tiles;
@@ -247,25 +303,26 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const int p0 = tile * RT;
     const int rows = min(RT, g.n_cand - p0);
 
-    const float* qbase = qp + (bh * g.n_cand) * (int64_t)D;
-    const float* kbase = kp + ((b * Hkv + g_kv) * g.n_cand) * (int64_t)D;
+    const int64_t prow = pooled_rows(g.n_cand);
+    const float* qbase = qp + bh * prow * D;
+    const float* kbase = kp + (b * Hkv + g_kv) * prow * D;
 
-    // ---- scores S[p0 + r][c] = <Qsum_(p0+r), Ksum_c> with fp32 MFMA 16x16x4
+    // ---- scores S[p0 + r][c] = <Qsum_(p0+r), Ksum_c> with fp32 MFMA 16x16x4;
+    // operands come straight from the tiled sums (1 KB per wave read)
     const int li = lane & 15, gq = lane >> 4;
+    const int n_ct = (int)(prow / 16);
     f4v a[RT / 16][KQ / 4];
 #pragma unroll
     for (int rt = 0; rt < RT / 16; ++rt) {
-        const int pr = min(p0 + rt * 16 + li, g.n_cand - 1);
-        const f4v* src = (const f4v*)(qbase + (int64_t)pr * D + gq * KQ);
+        const int tq = min(p0 / 16 + rt, n_ct - 1);
+        const f4v* src = (const f4v*)(qbase + (int64_t)tq * 16 * D) + lane;
 #pragma unroll
-        for (int c = 0; c < KQ / 4; ++c) a[rt][c] = src[c];
+        for (int c = 0; c < KQ / 4; ++c) a[rt][c] = src[c * 64];
     }
-    const int n_ct = (g.n_cand + 15) / 16;
     auto load_b = [&](int ct, f4v (&bv)[KQ / 4]) {
-        const int jc = min(ct * 16 + li, g.n_cand - 1);
-        const f4v* src = (const f4v*)(kbase + (int64_t)jc * D + gq * KQ);
+        const f4v* src = (const f4v*)(kbase + (int64_t)ct * 16 * D) + lane;
 #pragma unroll
-        for (int c = 0; c < KQ / 4; ++c) bv[c] = src[c];
+        for (int c = 0; c < KQ / 4; ++c) bv[c] = src[c * 64];
     };
     f4v bnext[KQ / 4];
     if (wave < n_ct) load_b(wave, bnext);
@@ -294,7 +351,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const int32_t w = g.w;
     auto compact_sparse = [&](int p, const uint8_t* keep_row) {
         const int32_t i = cand_block(g, p);
-        compact_row(g, lane, false, false, out.mask + (slice * nb + i) * nb,
+        compact_row(g, codes, vec4, lane, false, false, out.mask + (slice * nb + i) * nb,
                     out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
                     [&](int32_t j, int32_t code) {
                         return keep_row[code] != 0 || (w >= 0 && abs(j - i) <= w);
@@ -374,7 +431,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     for (int t = tile * WAVES + wave; t < g.n_other; t += n_tiles * WAVES) {
         const int32_t i = other_block(g, t);
         const int32_t cls = block_class(g, i);
-        compact_row(g, lane, cls == CLS_DROPPED, cls == CLS_PINNED,
+        compact_row(g, codes, vec4, lane, cls == CLS_DROPPED, cls == CLS_PINNED,
                     out.mask + (slice * nb + i) * nb, out.index + (slice * nb + i) * nb,
                     out.count + slice * nb + i, [](int32_t, int32_t) { return false; });
     }
@@ -386,6 +443,10 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
 // the window; k = n_cand gives the dense (layout-only) mask.  grid.y = slice.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
+    __shared__ int16_t s_code[kCodeTable];
+    const int16_t* codes = fill_codes(g, s_code);
+    __syncthreads();
+    const bool vec4 = (g.nb & 3) == 0 && ((uintptr_t)out.mask & 3u) == 0;
     const int lane = threadIdx.x & 63;
     const int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (i >= g.nb) return;
@@ -409,7 +470,7 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
         lo = __shfl(L + 1, 0);
     }
     const int32_t w = g.w;
-    compact_row(g, lane, code_i == -2, code_i == -1, out.mask + (slice * nb + i) * nb,
+    compact_row(g, codes, vec4, lane, code_i == -2, code_i == -1, out.mask + (slice * nb + i) * nb,
                 out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
                 [&](int32_t j, int32_t code) {
                     return (code >= lo && code < lo + kk) || (w >= 0 && abs(j - i) <= w);

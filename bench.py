@@ -70,12 +70,16 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="sdxl_bf16", choices=sorted(workloads.ALL))
-    p.add_argument("--layer", type=int, default=0, help="layer of the stacked workload")
+    p.add_argument("--layer", type=int, default=0, help="layer of the stacked workload (with --one-layer)")
+    p.add_argument("--one-layer", action="store_true",
+                   help="stacked workload: time one layer instead of all layers back to back")
+    p.add_argument("--no-cold", action="store_true", help="skip the cache-cold secondary timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
-    p.add_argument("--eager", action="store_true",
-                   help="launch every step from the host instead of replaying a captured HIP graph")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the step (and the per-call loops) as captured HIP graphs instead of "
+                        "launching every call from the host")
     return p.parse_args()
 
 
@@ -99,21 +103,135 @@ def selector_bytes(w, bm: hm.BlockMask, n_cand: int) -> float:
     return reads + writes
 
 
-def cpu_baseline(w, q, k, v, layout_segments, head_mask_np, flops_total):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, layers, flops_total, budget_s: float = 12.0):
+    """The fp64 oracle on this host's cores, on a bounded sample of the same
+    workload, scaled to the whole step.
+
+    `layers` is a list of (q, k, v, head_mask_np) on the host.  Selection runs
+    in full on every sampled layer; attention runs on every query row when
+    that fits the time budget, else on a seeded sample of rows (each row of
+    the masked-dense oracle costs the same), and its time is scaled by rows.
+    """
     import oracle
-    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
-    reps, t_total = 0, 0.0
-    while t_total < 5.0 and reps < 20:
+    rng = np.random.default_rng(0)
+    t_sel = t_att = 0.0
+    rows_done = rows_total = 0
+    for (q, k, v, hm_np) in layers:
+        q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
         t0 = time.perf_counter()
-        mask, _tie = oracle.select(q64, k64, w.block, layout_segments, w.budget, w.window_tokens)
-        oracle.attention(q64, k64, v64, w.block, mask, head_mask=head_mask_np)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    sec = t_total / reps
-    return {"value": flops_total / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"full {w.name} step (select + masked-dense attention on every row), "
-                      f"{reps} reps, {sec:.3f} s per step, fp64"}
+        mask, _tie = oracle.select(q64, k64, w.block, list(w.segments), w.budget, w.window_tokens)
+        t_sel += time.perf_counter() - t0
+        n_rows = w.B * w.H * w.N
+        rows_total += n_rows
+        # one row's cost, measured on a small probe, sizes the sample
+        probe = np.stack([rng.integers(0, w.B, 8), rng.integers(0, w.H, 8), rng.integers(0, w.N, 8)], 1)
+        t0 = time.perf_counter()
+        oracle.attention(q64, k64, v64, w.block, mask, head_mask=hm_np, rows=probe)
+        per_row = (time.perf_counter() - t0) / 8
+        want = int(max(64, min(n_rows, (budget_s / max(len(layers), 1)) / max(per_row, 1e-9))))
+        if want >= n_rows:
+            t0 = time.perf_counter()
+            oracle.attention(q64, k64, v64, w.block, mask, head_mask=hm_np)
+            t_att += time.perf_counter() - t0
+            rows_done += n_rows
+        else:
+            rows = np.stack([rng.integers(0, w.B, want), rng.integers(0, w.H, want),
+                             rng.integers(0, w.N, want)], 1)
+            t0 = time.perf_counter()
+            oracle.attention(q64, k64, v64, w.block, mask, head_mask=hm_np, rows=rows)
+            t_att += time.perf_counter() - t0
+            rows_done += want
+    sec = t_sel + t_att * rows_total / rows_done
+    full = rows_done == rows_total
+    return {"value": flops_total / sec / 1e12,
+            "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
+            "sample": (f"{len(layers)} layer(s) of {w.name}: selection in full, masked-dense fp64 attention on "
+                       + ("every query row" if full else
+                          f"{rows_done} of {rows_total} query rows (seeded), time scaled by rows")
+                       + f"; {t_sel + t_att:.1f} s measured, {sec:.2f} s per step extrapolated")}
+
+
+class Timer:
+    """Per-call GPU time of a call sequence.
+
+    `eager`: `reps` back-to-back host launches timed with HIP events on the
+    stream the kernels run on.  Otherwise the sequence is captured once into a
+    HIP graph holding `reps` copies and one replay is timed.
+    """
+
+    def __init__(self, dev, stream, eager: bool):
+        self.dev, self.stream, self.eager = dev, stream, eager
+
+    def warm(self, fn, reps: int, warmup: int) -> float:
+        for _ in range(warmup):
+            fn(self.stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            e0.record(self.stream)
+            for _ in range(reps):
+                fn(self.stream)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(self.dev)
+        cap.wait_stream(self.stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(reps):
+                    fn(cap)
+        self.stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            g.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def cold(self, fn, reps: int, scratch: torch.Tensor) -> float:
+        """Median time of one call after a 512 MiB scratch write that evicts
+        the L2 and the MALL (outside the timed region)."""
+        ts = []
+        for _ in range(reps):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            fn(self.stream)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+
+def stage_layers(w, layer_ids, dev):
+    """Q/K/V (device) and head masks of the given layers."""
+    layers = []
+    for l in layer_ids:
+        q, k, v = workloads.make_qkv(w, l)
+        if w.layers > 1:
+            hm_np = hm.head_mask(workloads.head_importance(w, l))
+        elif w.head_mask is not None:
+            hm_np = np.array(w.head_mask, np.uint8)
+        else:
+            hm_np = None
+        layers.append(dict(q=q, k=k, v=v, qd=q.to(dev), kd=k.to(dev), vd=v.to(dev), hm_np=hm_np,
+                           hmd=None if hm_np is None else torch.from_numpy(hm_np).to(dev)))
+    return layers
 
 
 def main():
@@ -125,53 +243,58 @@ def main():
     w = workloads.ALL[args.workload]
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    stack = w.layers > 1 and not args.one_layer
+    layer_ids = list(range(w.layers)) if stack else [args.layer]
+    layers = stage_layers(w, layer_ids, dev)
 
-    q, k, v = workloads.make_qkv(w, args.layer)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     layout = hm.Layout(w.block, list(w.segments), w.window_tokens)
-    head_mask_np = None
-    if w.layers > 1:
-        head_mask_np = hm.head_mask(workloads.head_importance(w, args.layer))
-    elif w.head_mask is not None:
-        head_mask_np = np.array(w.head_mask, np.uint8)
-    head_mask = None if head_mask_np is None else torch.from_numpy(head_mask_np).to(dev)
-
     _cls, n_cand = hm.layout_classes(layout, w.N)
     nb = w.nb
-    bm = hm.empty_block_mask(w.B, w.H, nb, dev)
+    L = len(layers)
+    bms = [hm.empty_block_mask(w.B, w.H, nb, dev) for _ in range(L)]
     bm_full = hm.empty_block_mask(w.B, w.H, nb, dev)
     ws = torch.empty(hm.select_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.block, w.D),
                      dtype=torch.uint8, device=dev)
-    out = torch.empty_like(qd)
+    outs = [torch.empty_like(ly["qd"]) for ly in layers]
     stream = torch.cuda.current_stream(dev)
+    timer = Timer(dev, stream, eager=not args.graph)
 
-    def step():
-        hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream)
-        hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=stream)
+    def select(i, st, budget=None, out=None):
+        ly = layers[i]
+        hm.select(ly["qd"], ly["kd"], layout, w.budget if budget is None else budget,
+                  out=bms[i] if out is None else out, workspace=ws, stream=st)
 
+    def forward(i, st, bm=None):
+        ly = layers[i]
+        hm.forward(ly["qd"], ly["kd"], ly["vd"], bms[i] if bm is None else bm, ly["hmd"], out=outs[i], stream=st)
+
+    def step(st):
+        for i in range(L):
+            select(i, st)
+            forward(i, st)
+
+    # ---- whole-step throughput: K steps on the host clock, synchronised on
+    # both sides.  Every call is launched from the host (the host runs ahead
+    # of the GPU); --graph captures the step once and replays it instead.  On
+    # MI355X the replayed kernels start with a cold L2, so host launches are
+    # the faster default here.
     for _ in range(args.warmup):
-        step()
+        step(stream)
     torch.cuda.synchronize()
-    # One step = select + forward.  By default the step is captured once as a
-    # HIP graph and replayed, so the host's per-call launch cost stays out of
-    # the GPU timeline; --eager launches every call from the host.
-    run_step = step
-    graph = None
-    if not args.eager:
+    run_step = lambda: step(stream)
+    if args.graph:
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream(dev)
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             with torch.cuda.graph(graph, stream=cap):
-                hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=cap)
-                hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=cap)
+                step(cap)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
         run_step = graph.replay
         for _ in range(args.warmup):
             run_step()
         torch.cuda.synchronize()
-    # whole-step throughput: K steps, host clock, synchronised on both sides
     t0 = time.perf_counter()
     for _ in range(args.steps):
         run_step()
@@ -179,37 +302,53 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    def timed_launches(fn):
-        """Average launch time of fn over K back-to-back launches, HIP events
-        recorded on the stream the kernels run on."""
-        for _ in range(args.warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    sel_ms = timed_launches(lambda: hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream))
-    fwd_ms = timed_launches(lambda: hm.forward(qd, kd, vd, bm, head_mask, out=out, stream=stream))
+    # ---- per-call figures (layer 0), warm: back-to-back calls in one graph
+    reps = max(1, min(args.steps, 50))
+    sel_ms = timer.warm(lambda st: select(0, st), reps, args.warmup)
+    fwd_ms = timer.warm(lambda st: forward(0, st), reps, args.warmup)
     # the same attention kernel at full density (budget 1.0: same layout and head mask)
-    hm.select(qd, kd, layout, 1.0, out=bm_full, workspace=ws, stream=stream)
-    dense_ms = timed_launches(lambda: hm.forward(qd, kd, vd, bm_full, head_mask, out=out, stream=stream))
+    select(0, stream, budget=1.0, out=bm_full)
+    dense_ms = timer.warm(lambda st: forward(0, st, bm=bm_full), reps, args.warmup)
+    # cold: L2 and MALL evicted before each call (secondary figures)
+    cold = None
+    if not args.no_cold:
+        scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB
+        cold = {"selector_ms": timer.cold(lambda st: select(0, st), 11, scratch),
+                "attention_ms": timer.cold(lambda st: forward(0, st), 11, scratch),
+                "note": "median of 11 single calls, each after a 512 MiB scratch write"}
+        del scratch
 
     # the step's own result, outside every timed region
-    hm.select(qd, kd, layout, w.budget, out=bm, workspace=ws, stream=stream)
+    for i in range(L):
+        select(i, stream)
     torch.cuda.synchronize()
-    flops = kept_flops(bm.count, head_mask, w.block, w.D, w.H)
-    flops_dense = kept_flops(bm_full.count, head_mask, w.block, w.D, w.H)
-    sel_bytes = selector_bytes(w, bm, n_cand)
-    attn_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    flops_layers = [kept_flops(bms[i].count, layers[i]["hmd"], w.block, w.D, w.H) for i in range(L)]
+    flops = sum(flops_layers)
+    flops0 = flops_layers[0]
+    flops_dense0 = kept_flops(bm_full.count, layers[0]["hmd"], w.block, w.D, w.H)
+    sel_bytes = selector_bytes(w, bms[0], n_cand)
+    attn_tflops = flops0 / (fwd_ms * 1e-3) / 1e12
     sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
+
+    radial = None
+    if w.radial:
+        # the layout-only band control at the selector's density: the same k
+        bm_rad = hm.radial(layout, w.N, w.budget, B=1, H=1, device=dev)
+        rad_ms = timer.warm(lambda st: hm.radial(layout, w.N, w.budget, B=1, H=1, out=bm_rad, stream=st),
+                            reps, args.warmup)
+        rad_fwd_ms = timer.warm(lambda st: forward(0, st, bm=bm_rad), reps, args.warmup)
+        torch.cuda.synchronize()
+        rad_flops = kept_flops(bm_rad.count, layers[0]["hmd"], w.block, w.D, w.H)
+        radial = {"radial_ms": rad_ms, "attention_ms": rad_fwd_ms, "flops": rad_flops,
+                  "tflops": rad_flops / (rad_fwd_ms * 1e-3) / 1e12, "k": bm_rad.k}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q, k, v, list(w.segments), head_mask_np, flops)
+        sample_ids = [0] if not stack else [0, w.layers // 3, 2 * w.layers // 3, w.layers - 1]
+        sample = [(layers[i]["q"], layers[i]["k"], layers[i]["v"], layers[i]["hm_np"]) for i in sample_ids]
+        # kept FLOPs of the sampled layers, so value compares like with like
+        flops_sample = sum(flops_layers[i] for i in sample_ids)
+        cpu = cpu_baseline(w, sample, flops_sample)
 
     if args.calibrate_copy:
         # an elementwise kernel that reads 256 MiB and writes 256 MiB: the known
@@ -220,6 +359,7 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
+    hmask0 = layers[0]["hm_np"]
     res = {
         "metric": "block-sparse attn TFLOP/s on kept blocks & speedup vs dense at 30% budget",
         "value": flops / (ms_per_step * 1e-3) / 1e12,
@@ -233,22 +373,25 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded; clustered Q/K for image workloads)",
-        "step_launch": "eager" if args.eager else "hip graph replay",
+        "step_launch": "hip graph replay" if args.graph else "host launches",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
-                   "block": w.block, "budget": w.budget, "k": bm.k, "layer": args.layer,
+                   "block": w.block, "budget": w.budget, "k": bms[0].k,
+                   "layers": L, "layer": layer_ids[0] if L == 1 else None,
                    "segments": [list(s) for s in w.segments], "window_tokens": w.window_tokens,
-                   "active_heads": int(head_mask_np.sum()) if head_mask_np is not None else w.H,
+                   "active_heads": int(hmask0.sum()) if hmask0 is not None else w.H,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel" if w.dtype == "bf16" else "attn_vec_kernel",
                      "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(w.name),
                      "traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
-                     "flops_per_launch": flops, "avg_launch_ms": fwd_ms},
+                     "flops_per_launch": flops0, "avg_launch_ms": fwd_ms},
         "selector": {"bound": "hbm", "achieved": sel_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": sel_gbps / HBM_PEAK_GBPS, "bytes_per_call": sel_bytes, "avg_call_ms": sel_ms},
         "speedup_vs_dense": {"attention": dense_ms / fwd_ms, "step": dense_ms / (sel_ms + fwd_ms),
-                             "dense_attention_ms": dense_ms, "dense_flops": flops_dense,
-                             "ideal": flops_dense / flops},
+                             "dense_attention_ms": dense_ms, "dense_flops": flops_dense0,
+                             "ideal": flops_dense0 / flops0},
+        "cold": cold,
+        "radial": radial,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "host": platform.node()},

@@ -454,20 +454,23 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
     const int64_t nb = g.nb;
     const int32_t code_i = column_code(g, i);
 
+    // The k nearest candidates by (|i - j|, j) are the run of candidate
+    // positions [lo, lo + k) that holds the diagonal p.  Against the run one
+    // step to the right it trades candidate lo for lo + k, and the right one
+    // is better exactly when lo + k is strictly nearer; along lo that test
+    // flips once from true to false, so lo is the first position where it is
+    // false (binary search, wave-uniform).
     int32_t lo = 0, kk = g.n_cand;
     if (code_i >= 0 && !g.is_dense) {
         kk = g.k;
-        int32_t L = code_i - 1, R = code_i + 1;
-        if (lane == 0) {
-            for (int taken = 1; taken < kk; ++taken) {
-                bool take_left;
-                if (L < 0) take_left = false;
-                else if (R >= g.n_cand) take_left = true;
-                else take_left = (i - cand_block(g, L)) <= (cand_block(g, R) - i);
-                if (take_left) --L; else ++R;
-            }
+        const int32_t p = code_i;
+        int32_t a = max(0, p - kk + 1), b = min(p, g.n_cand - kk);   // lo in [a, b]
+        while (a < b) {
+            const int32_t m = (a + b) >> 1;
+            const bool right = (cand_block(g, m + kk) - i) < (i - cand_block(g, m));
+            if (right) a = m + 1; else b = m;
         }
-        lo = __shfl(L + 1, 0);
+        lo = a;
     }
     const int32_t w = g.w;
     compact_row(g, codes, vec4, lane, code_i == -2, code_i == -1, out.mask + (slice * nb + i) * nb,

@@ -119,6 +119,10 @@ def test_mask_density(cuda):
      64 * 40, 64, 0.25, 300),
     ((), 32 * 9, 32, 0.5, 0),
     ((("text", 128), ("padding", 384), ("video", 64 * 200)), 512 + 64 * 200, 64, 1.0, 0),
+    # candidates with a one-block gap: equal distances on both sides of the gap
+    ((("image", 64 * 3), ("text", 64), ("image", 64 * 3)), 64 * 7, 64, 0.5, 0),
+    ((("image", 32 * 7), ("audio", 32 * 2), ("video", 32 * 11), ("padding", 32), ("image", 32 * 9)),
+     32 * 30, 32, 0.4, 0),
 ])
 def test_radial_small(cuda, segs, N, block, density, window):
     lay = hm.Layout(block, list(segs), window)

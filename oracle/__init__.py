@@ -59,7 +59,7 @@ def _load():
     lib.orc_radial.argtypes = [i64, i32, p, dbl, i32, p]
     lib.orc_radial.restype = ctypes.c_int
     lib.orc_attention_rows.argtypes = [p, p, p, i64, i64, i64, i64, i64, i32, p, i64, i64, p,
-                                       dbl, i64, p, p, p, p]
+                                       dbl, i64, p, p, p, p, p]
     lib.orc_attention_rows.restype = ctypes.c_int
     lib.orc_head_mask.argtypes = [p, i64, dbl, i64, p]
     lib.orc_head_mask.restype = ctypes.c_int
@@ -132,13 +132,15 @@ def radial(N: int, block: int, segments, density: float, window_tokens: int = 0)
 
 
 def attention(q, k, v, block: int, mask, head_mask=None, scale: float | None = None,
-              rows=None) -> np.ndarray:
+              rows=None, key_mask=None) -> np.ndarray:
     """Attention under an explicit -inf block mask (SD.Next flex-consumer paragraph).
 
     q [B,H,N,D]; k, v [B,Hkv,N,D]; mask uint8 [mB,mH,NB,NB] (mB in {1,B}, mH in
     {1,H}) or [NB,NB] (shared).  head_mask uint8 [H] or None.  rows: None for
     every row (returns [B,H,N,D]) or an int array [R,3] of (b, h, t) triples
-    (returns [R,D]).
+    (returns [R,D]).  key_mask: None or uint8 [B,N] (or [N], shared by the
+    batch): keys where it is 0 are -inf too (SD.Next sparse-stage paragraph,
+    token mask composed with the block mask).
     """
     q = _f64(q)
     k = _f64(k)
@@ -161,10 +163,14 @@ def attention(q, k, v, block: int, mask, head_mask=None, scale: float | None = N
     rh = np.ascontiguousarray(rows_arr[:, 1], dtype=np.int64)
     rt = np.ascontiguousarray(rows_arr[:, 2], dtype=np.int64)
     R = rows_arr.shape[0]
+    km = None
+    if key_mask is not None:
+        km = np.ascontiguousarray(np.broadcast_to(np.asarray(key_mask, dtype=np.uint8), (B, N)))
     out = np.zeros((R, D), dtype=np.float64)
     rc = _load().orc_attention_rows(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, D, block, _ptr(m),
                                     mB, mH, None if hm is None else _ptr(hm), float(scale), R,
-                                    _ptr(rb), _ptr(rh), _ptr(rt), _ptr(out))
+                                    _ptr(rb), _ptr(rh), _ptr(rt), _ptr(out),
+                                    None if km is None else _ptr(km))
     if rc != 0:
         raise ValueError("bad attention arguments")
     if rows is None:

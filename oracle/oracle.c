@@ -281,13 +281,16 @@ int orc_radial(int64_t NB, int32_t block, const uint8_t* cls, double density,
 /* key's block is not kept, softmax with max subtraction, then the weighted  */
 /* sum of V.  A row whose logits are all -inf, and every row of a masked     */
 /* head, is exactly 0.                                                       */
+/* key_mask: [B][N] per-token key mask or NULL [SDN sparse-stage paragraph:  */
+/* a backend declaring masked_block takes the token attention mask and the   */
+/* block mask together]; key j of batch b is -inf as well where it is 0.     */
 /* ------------------------------------------------------------------------ */
 int orc_attention_rows(const double* q, const double* k, const double* v,
                        int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D,
                        int32_t block, const uint8_t* mask, int64_t mB, int64_t mH,
                        const uint8_t* head_mask, double scale,
                        int64_t R, const int64_t* rb, const int64_t* rh, const int64_t* rt,
-                       double* out)
+                       double* out, const uint8_t* key_mask)
 {
     if (Hkv <= 0 || H % Hkv != 0 || N % block != 0) return -1;
     if (!(mB == 1 || mB == B) || !(mH == 1 || mH == H)) return -1;
@@ -311,6 +314,7 @@ int orc_attention_rows(const double* q, const double* k, const double* v,
             double m = -INFINITY;
             for (int64_t j = 0; j < N; ++j) {
                 if (!mrow[j / block]) { logit[j] = -INFINITY; continue; }
+                if (key_mask && !key_mask[bb * N + j]) { logit[j] = -INFINITY; continue; }
                 double s = 0.0;
                 for (int64_t d = 0; d < D; ++d) s += qt[d] * kh[j * D + d];
                 logit[j] = scale * s;

@@ -119,6 +119,77 @@ def test_every_block_mask_matches_gathered_sdpa(nb):
     assert worst <= 1e-12
 
 
+# ---- per-token key mask composed with the block mask (SD.Next sparse-stage
+# paragraph: a masked_block backend takes the token mask and block mask together)
+
+def test_key_mask_equals_sdpa_boolean_mask():
+    B, H, N, D, block = 2, 3, 96, 8, 32
+    q, k, v = rnd((B, H, N, D), 40), rnd((B, H, N, D), 41), rnd((B, H, N, D), 42)
+    km = (np.random.default_rng(43).random((B, N)) < 0.7).astype(np.uint8)
+    km[:, 0] = 1
+    out = oracle.attention(q, k, v, block, np.ones((3, 3), np.uint8), key_mask=km)
+    am = torch.from_numpy(km.astype(bool))[:, None, None, :]
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=am).numpy()
+    assert np.abs(out - ref).max() <= 1e-12
+
+
+def test_key_mask_and_block_mask_compose_as_gathered_sdpa():
+    # each query block attends to the keys that are both in a kept block and
+    # unmasked: gather exactly those and run sdpa on them
+    B, H, N, D, block = 2, 2, 64, 8, 16
+    nb = N // block
+    q, k, v = rnd((B, H, N, D), 44), rnd((B, H, N, D), 45), rnd((B, H, N, D), 46)
+    rng = np.random.default_rng(47)
+    bm = (rng.random((nb, nb)) < 0.6).astype(np.uint8)
+    np.fill_diagonal(bm, 1)
+    km = (rng.random((B, N)) < 0.75).astype(np.uint8)
+    km[:, ::block] = 1                      # every block keeps a live key
+    out = oracle.attention(q, k, v, block, bm, key_mask=km)
+    for b in range(B):
+        for i in range(nb):
+            keys = [j for j in range(N) if bm[i, j // block] and km[b, j]]
+            ref = sdpa64(np.ascontiguousarray(q[b:b + 1, :, i * block:(i + 1) * block]),
+                         np.ascontiguousarray(k[b:b + 1][:, :, keys]), np.ascontiguousarray(v[b:b + 1][:, :, keys]))
+            assert np.abs(out[b:b + 1, :, i * block:(i + 1) * block] - ref).max() <= 1e-12
+
+
+def test_masked_keys_never_reach_the_output():
+    B, H, N, D, block = 1, 2, 64, 8, 32
+    q, k, v = rnd((B, H, N, D), 48), rnd((B, H, N, D), 49), rnd((B, H, N, D), 50)
+    km = np.ones((B, N), np.uint8)
+    km[0, 5:40] = 0
+    a = oracle.attention(q, k, v, block, np.ones((2, 2), np.uint8), key_mask=km)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 5:40] = 1e3 * rnd((B, H, 35, D), 51)
+    v2[:, :, 5:40] = -7.0
+    b2 = oracle.attention(q, k2, v2, block, np.ones((2, 2), np.uint8), key_mask=km)
+    assert np.array_equal(a, b2)
+
+
+def test_key_mask_of_whole_block_equals_block_mask_column():
+    B, H, N, D, block = 1, 2, 96, 8, 32
+    q, k, v = rnd((B, H, N, D), 52), rnd((B, H, N, D), 53), rnd((B, H, N, D), 54)
+    km = np.ones((B, N), np.uint8)
+    km[:, 32:64] = 0
+    bm = np.ones((3, 3), np.uint8)
+    bm[:, 1] = 0
+    a = oracle.attention(q, k, v, block, np.ones((3, 3), np.uint8), key_mask=km)
+    b = oracle.attention(q, k, v, block, bm)
+    assert np.array_equal(a, b)
+
+
+def test_rows_whose_kept_keys_are_all_masked_are_zero():
+    B, H, N, D, block = 1, 1, 64, 8, 32
+    q, k, v = rnd((B, H, N, D), 55), rnd((B, H, N, D), 56), rnd((B, H, N, D), 57)
+    bm = np.array([[1, 0], [1, 1]], np.uint8)
+    km = np.ones((B, N), np.uint8)
+    km[:, :32] = 0                          # query block 0 keeps only block 0: all masked
+    out = oracle.attention(q, k, v, block, bm, key_mask=km)
+    assert np.all(out[:, :, :32] == 0.0)
+    assert np.abs(out[:, :, 32:]).max() > 0
+
+
 def test_sampled_rows_match_full_rows():
     q, k, v = rnd((2, 3, 96, 8), 16), rnd((2, 3, 96, 8), 17), rnd((2, 3, 96, 8), 18)
     rng = np.random.default_rng(19)

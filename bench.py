@@ -342,6 +342,20 @@ def main():
         radial = {"radial_ms": rad_ms, "attention_ms": rad_fwd_ms, "flops": rad_flops,
                   "tflops": rad_flops / (rad_fwd_ms * 1e-3) / 1e12, "k": bm_rad.k}
 
+    # per-token key mask composed with the block mask (bsattn_forward_masked):
+    # all keys live, and the last 1/16 of each batch's keys masked
+    km_live = torch.ones(w.B, w.N, dtype=torch.uint8, device=dev)
+    km_tail = km_live.clone()
+    km_tail[:, w.N - w.N // 16:] = 0
+    ly0 = layers[0]
+    key_mask = {
+        "all_live_ms": timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
+                                                        out=outs[0], stream=st, key_mask=km_live), reps, args.warmup),
+        "tail_masked_ms": timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
+                                                           out=outs[0], stream=st, key_mask=km_tail), reps, args.warmup),
+        "note": "bsattn_forward_masked on the step's block mask; tail = last N/16 keys of each batch masked",
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         sample_ids = [0] if not stack else [0, w.layers // 3, 2 * w.layers // 3, w.layers - 1]
@@ -392,6 +406,7 @@ def main():
                              "ideal": flops_dense0 / flops0},
         "cold": cold,
         "radial": radial,
+        "key_mask": key_mask,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "host": platform.node()},

@@ -59,7 +59,7 @@ class _BlockMask(ctypes.Structure):
 
 EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
-           "bsattn_head_mask", "bsattn_mask_density"]
+           "bsattn_forward_masked", "bsattn_head_mask", "bsattn_mask_density"]
 
 _lib = None
 
@@ -90,6 +90,9 @@ def load_library(path: str = LIB_PATH):
     lib.bsattn_forward.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                    ctypes.POINTER(_Tensor), ctypes.POINTER(_BlockMask), P,
                                    ctypes.c_float, ctypes.POINTER(_Tensor), P]
+    lib.bsattn_forward_masked.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                          ctypes.POINTER(_Tensor), ctypes.POINTER(_BlockMask), P, P, i64,
+                                          ctypes.c_float, ctypes.POINTER(_Tensor), P]
     lib.bsattn_head_mask.argtypes = [P, i32, dbl, i32, P]
     lib.bsattn_mask_density.argtypes = [ctypes.POINTER(_BlockMask), P, ctypes.POINTER(dbl)]
     for name in EXPORTS[1:]:
@@ -218,8 +221,12 @@ def radial(layout: Layout, N: int, density: float, *, B: int = 1, H: int = 1, de
 
 
 def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale: float = 0.0,
-            *, out=None, stream=None):
-    """bsattn_forward: attention over the kept blocks; masked heads give zeros."""
+            *, out=None, stream=None, key_mask=None):
+    """bsattn_forward: attention over the kept blocks; masked heads give zeros.
+
+    key_mask: optional uint8 device tensor [B, N] (or [N], shared by the
+    batch); keys where it is 0 are masked in every row (bsattn_forward_masked).
+    """
     import torch
     lib = load_library()
     if out is None:
@@ -233,10 +240,23 @@ def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale:
         if head_mask.numel() != q.shape[1] or not head_mask.is_contiguous():
             raise BsattnError(3, "bsattn_forward", "head_mask must hold one byte per query head")
         hm = head_mask.data_ptr()
-    st = lib.bsattn_forward(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
-                            None if bm is None else ctypes.byref(bm), hm, float(scale),
-                            ctypes.byref(to), _stream(q.device, stream))
-    _check(st, "bsattn_forward")
+    if key_mask is None:
+        st = lib.bsattn_forward(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                None if bm is None else ctypes.byref(bm), hm, float(scale),
+                                ctypes.byref(to), _stream(q.device, stream))
+        _check(st, "bsattn_forward")
+        return out
+    if key_mask.dtype != torch.uint8 or not key_mask.is_cuda:
+        raise BsattnError(2, "bsattn_forward_masked", "key_mask must be a uint8 device tensor")
+    if key_mask.shape[-1] != q.shape[2] or key_mask.stride(-1) != 1 or key_mask.dim() not in (1, 2):
+        raise BsattnError(3, "bsattn_forward_masked", "key_mask must be [B, N] or [N] with unit key stride")
+    if key_mask.dim() == 2 and key_mask.shape[0] != q.shape[0]:
+        raise BsattnError(3, "bsattn_forward_masked", "key_mask batch must match q")
+    km_sb = 0 if key_mask.dim() == 1 or key_mask.shape[0] == 1 else key_mask.stride(0)
+    st = lib.bsattn_forward_masked(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                   None if bm is None else ctypes.byref(bm), hm, key_mask.data_ptr(),
+                                   int(km_sb), float(scale), ctypes.byref(to), _stream(q.device, stream))
+    _check(st, "bsattn_forward_masked")
     return out
 
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // with its own LDS stages, and the groups' partial softmax states are merged
 // through LDS at the end.  More wavefronts per query block hide more latency
 // when the grid alone cannot fill the chip.
-template <int D, int KT, int SPLIT, int WPE, bool HOIST, bool LAUNDER, bool VSINGLE>
+template <int D, int KT, int SPLIT, int WPE, bool HOIST, bool LAUNDER, bool VSINGLE, bool KMASK>
 __global__ __launch_bounds__(128 * SPLIT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
@@ -112,6 +112,7 @@ void attn_mfma_kernel(AttnArgs a) {
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
     static_assert(SPLIT == 1 || SPLIT * TILE * 2 >= D * 128, "merge buffer fits in one stage object");
     static_assert(!(VSINGLE && HOIST), "a single V stage is read only after its own barrier");
+    static_assert(!KMASK || KT == 32, "key-mask words cover one 32-key stage");
 
     // one LDS object per stage (holding every group's tile): distinct objects
     // let the compiler see that the reads of one stage never alias the loads
@@ -208,12 +209,24 @@ void attn_mfma_kernel(AttnArgs a) {
                 (const __attribute__((address_space(1))) void*)(vt + voff[i]),
                 (__attribute__((address_space(3))) void*)(Vd + (i * 128 + wq * 64) * 8), 16, 0, 0);
     };
+    // KMASK: lanes 0..31 fetch the mask bytes of the 32 keys of a stage with
+    // its K tile (after its V); at the stage a ballot turns them into one
+    // wave-uniform 32-bit word.
+    const uint8_t* kmbase = KMASK ? a.key_mask + (int64_t)b * a.km_sb : nullptr;
+    uint32_t km_next = 1u;
+    auto issue_m = [&](int t) {
+        if constexpr (KMASK) {
+            const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+            km_next = lane < 32 ? (uint32_t)kmbase[row0 + lane] : 1u;
+        }
+    };
     // With VSINGLE the group has one V tile: V of stage t is loaded after the
     // stage's first barrier (every wave is past the previous P V) and waited
     // for at a second barrier before this stage's P V, while K stays double
     // buffered.  This keeps the workgroup's LDS small enough for five
     // workgroups per CU.
     if (Tg > 0) {
+        issue_m(0);
         issue_k(0, K0 + grp * TILE);
         if constexpr (!VSINGLE) issue_v(0, V0 + grp * TILE);
     }
@@ -250,14 +263,18 @@ void attn_mfma_kernel(AttnArgs a) {
     auto stage = [&](int t, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
         wait_vmcnt<0>();
         __syncthreads();
+        // this stage's key-mask word (wave-uniform); all ones without KMASK
+        uint32_t kw = 0xffffffffu;
+        if constexpr (KMASK) kw = (uint32_t)__ballot(km_next != 0u);
         if constexpr (VSINGLE) {
             if (t < Tg) issue_v(t, V0 + grp * TILE);
-            if (t + 1 < Tg) issue_k(t + 1, Kn);
+            if (t + 1 < Tg) { issue_m(t + 1); issue_k(t + 1, Kn); }
         } else if (t + 1 < Tg) {
+            issue_m(t + 1);
             issue_k(t + 1, Kn);
             issue_v(t + 1, Vn);
         }
-        if (t >= Tg) {
+        if (t >= Tg || (KMASK && kw == 0u)) {   // no work, or every key of the stage masked
             if constexpr (VSINGLE) __syncthreads();   // the stage's second barrier
             return;
         }
@@ -306,6 +323,16 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][ks], qf[ks], sacc[kt], 0, 0, 0);
+        }
+        if constexpr (KMASK) {
+            // masked keys of a partly masked stage: -inf scores.  Element r of
+            // lane half hl holds key (r & 7) | (hl << 3) | ((r >> 3) << 4).
+            if (kw != 0xffffffffu) {
+                const uint32_t wl = kw >> (8 * hl);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (!((wl >> ((r & 7) | ((r >> 3) << 4))) & 1u)) sacc[0][r] = -INFINITY;
+            }
         }
 
         // online softmax with lazy rescaling; the row maximum as a tree of
@@ -399,7 +426,9 @@ void attn_mfma_kernel(AttnArgs a) {
         // without blocks has m = -inf and contributes exp2(-inf) = 0
         const float m1 = pml[lane], l1 = pml[64 + lane];
         const float m = fmaxf(m_run, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+        // with a key mask a group (or both) may have seen no live key: m = -inf
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -408,7 +437,8 @@ void attn_mfma_kernel(AttnArgs a) {
     }
 
     // normalise and store: oacc[dt][r] = O[query][32*dt + 8*(r/4) + 4*hl + r%4]
-    const float inv = 1.f / pair_sum32(l_run);
+    const float l_tot = pair_sum32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // 0: every kept key masked
     uint16_t* orow = obase + (int64_t)(32 * wq + ql) * a.o_sn;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -460,14 +490,22 @@ void attn_mfma_kernel(AttnArgs a) {
 #define BSATTN_D128_HOIST true
 #endif
 
-hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {
+template <bool KMASK>
+static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
     const dim3 grid((unsigned)padded);
     if (D == 128)
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, BSATTN_D128_WPE, BSATTN_D128_HOIST, BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE>,
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, BSATTN_D128_WPE, BSATTN_D128_HOIST,
+                                       BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
-    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, BSATTN_D64_WPE, BSATTN_D64_HOIST, BSATTN_D64_LAUNDER, BSATTN_D64_VSINGLE>,
+    // the masked variant needs a few more registers: one wave less per SIMD
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? 4 : BSATTN_D64_WPE, BSATTN_D64_HOIST,
+                                   BSATTN_D64_LAUNDER, BSATTN_D64_VSINGLE, KMASK>,
                   grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {
+    return a.key_mask != nullptr ? launch_attn_mfma_t<true>(a, D, s) : launch_attn_mfma_t<false>(a, D, s);
 }
 
 }  // namespace bsattn

@@ -38,6 +38,7 @@ template <typename T, int D, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void attn_vec_kernel(AttnArgs a) {
     __shared__ float Ks[BLOCK][D];
     __shared__ float Vs[BLOCK][D];
+    __shared__ float Bs[BLOCK];        // 0 for a live key, -inf for a masked one
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(BLOCK) void attn_vec_kernel(AttnArgs a) {
         const T* kr = kbase + ((int64_t)kb * BLOCK + t) * a.k.sn;
         const T* vr = vbase + ((int64_t)kb * BLOCK + t) * a.v.sn;
         for (int d = 0; d < D; ++d) { Ks[t][d] = load_elem<T>(kr + d); Vs[t][d] = load_elem<T>(vr + d); }
+        Bs[t] = (a.key_mask == nullptr || a.key_mask[b * a.km_sb + (int64_t)kb * BLOCK + t] != 0) ? 0.f : -INFINITY;
         __syncthreads();
 
         // pass 1: block max of the scaled scores; pass 2 recomputes each score
@@ -86,8 +88,9 @@ __global__ __launch_bounds__(BLOCK) void attn_vec_kernel(AttnArgs a) {
             float acc = 0.f;
 #pragma unroll
             for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[j][d], acc);
-            mx = fmaxf(mx, acc * a.scale);
+            mx = fmaxf(mx, acc * a.scale + Bs[j]);
         }
+        if (mx == -INFINITY) continue;   // every key of this block masked
         const float m_new = fmaxf(m_run, mx);
         const float alpha = expf(m_run - m_new);
         m_run = m_new;
@@ -98,14 +101,14 @@ __global__ __launch_bounds__(BLOCK) void attn_vec_kernel(AttnArgs a) {
             float acc = 0.f;
 #pragma unroll
             for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[j][d], acc);
-            const float p = expf(acc * a.scale - m_new);
+            const float p = expf(acc * a.scale + Bs[j] - m_new);
             psum += p;
 #pragma unroll
             for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vs[j][d], o[d]);
         }
         l_run = l_run * alpha + psum;
     }
-    const float inv = 1.f / l_run;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // 0: every kept key masked
     for (int d = 0; d < D; ++d) store_elem<T>(orow + d, o[d] * inv);
 }
 

@@ -253,6 +253,14 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
                              const bsattn_tensor* v, const bsattn_block_mask* mask,
                              const uint8_t* head_mask, float scale, bsattn_tensor* out,
                              void* stream) {
+    return bsattn_forward_masked(q, k, v, mask, head_mask, nullptr, 0, scale, out, stream);
+}
+
+bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor* k,
+                                    const bsattn_tensor* v, const bsattn_block_mask* mask,
+                                    const uint8_t* head_mask, const uint8_t* key_mask,
+                                    int64_t key_mask_stride_b, float scale, bsattn_tensor* out,
+                                    void* stream) {
     bsattn_status st;
     if ((st = check_tensor(q)) != BSATTN_OK) return st;
     if ((st = check_tensor(k)) != BSATTN_OK) return st;
@@ -276,6 +284,8 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
             return BSATTN_ERR_SHAPE;
     }
     if (!(std::isfinite(scale))) return BSATTN_ERR_BUDGET;
+    if (key_mask != nullptr && (key_mask_stride_b < 0 || (key_mask_stride_b > 0 && key_mask_stride_b < q->N)))
+        return BSATTN_ERR_STRIDE;
 
     AttnArgs a;
     a.q = view_of(q);
@@ -295,6 +305,8 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
     a.count = mask ? mask->count : nullptr;
     a.index = mask ? mask->index : nullptr;
     a.head_mask = head_mask;
+    a.key_mask = key_mask;
+    a.km_sb = key_mask ? key_mask_stride_b : 0;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     a.n_work = (int64_t)a.B * a.H * a.nqb;
 

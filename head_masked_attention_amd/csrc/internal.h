@@ -15,6 +15,8 @@ struct AttnArgs {
     const int32_t* count;        // NULL = dense (every block kept)
     const int32_t* index;
     const uint8_t* head_mask;    // NULL = every head active
+    const uint8_t* key_mask;     // NULL = every key live; else key_mask[b * km_sb + j]
+    int64_t km_sb;               // batch stride of key_mask (0 = shared)
     float scale;                 // softmax scale (> 0)
     int64_t n_work;              // B * H * nqb workgroups of real work
 };

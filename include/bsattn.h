@@ -224,6 +224,25 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
                              bsattn_tensor* out, void* stream);
 
 /*
+ * bsattn_forward with a per-token key mask composed with the block mask
+ * (SD.Next sparse-stage paragraph: a backend declaring masked_block takes the
+ * token attention mask and the block mask together).
+ *  key_mask: device uint8, key_mask[b * key_mask_stride_b + j] for key token
+ *        j of batch b; 0 masks the key (its logit is -inf in every row), any
+ *        other value keeps it.  key_mask_stride_b >= N, or 0 for one mask
+ *        shared by the batch.  NULL behaves exactly as bsattn_forward.
+ *  A row whose kept keys are all masked is written as 0.  Everything else,
+ *  including errors, as bsattn_forward; BSATTN_ERR_STRIDE when
+ *  0 < key_mask_stride_b < N.  Caller owns the mask; it is read by the
+ *  enqueued kernel only.
+ */
+bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor* k,
+                                    const bsattn_tensor* v, const bsattn_block_mask* mask,
+                                    const uint8_t* head_mask, const uint8_t* key_mask,
+                                    int64_t key_mask_stride_b, float scale,
+                                    bsattn_tensor* out, void* stream);
+
+/*
  * Per-layer head mask (haagenti_sparse AttentionMask / MaskBuilder with
  * DEFAULT_SPARSITY and MIN_ACTIVE_HEADS): skip floor(sparsity * H) heads but
  * keep at least min(H, min_active); the kept heads are those with the highest

@@ -192,6 +192,19 @@ def test_forward_validation(lib):
         assert st == code, (over, st)
 
 
+def test_forward_masked_validation(lib):
+    def call(km, sb, **over):
+        args = dict(q=tensor(), k=tensor(), v=tensor(), m=bmask(), out=tensor())
+        args.update(over)
+        return lib.bsattn_forward_masked(ctypes.byref(args["q"]), ctypes.byref(args["k"]),
+                                         ctypes.byref(args["v"]), ctypes.byref(args["m"]), None, km, sb,
+                                         0.0, ctypes.byref(args["out"]), None)
+    assert call(FAKE, 100) == 4                # batch stride shorter than N = 256
+    assert call(FAKE, -256) == 4
+    assert call(FAKE, 256, q=tensor(data=0)) == 1      # tensor checks come first
+    assert call(FAKE, 0, out=tensor(dtype=B_.F32)) == 2
+
+
 def test_radial_and_density_validation(lib):
     lay, _k = layout()
     out = bmask()

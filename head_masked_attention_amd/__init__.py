@@ -6,13 +6,25 @@ memory and streams) into the C calls.
 """
 from ._binding import (  # noqa: F401
     BF16,
+    DECLINE_CAUSAL,
+    DECLINE_DISABLED,
+    DECLINE_EXCLUDED,
+    DECLINE_NO_BACKEND,
+    DECLINE_NOT_SELF,
+    DECLINE_SHORT,
+    DECLINE_TOKEN_MASK,
+    DEFAULT_MIN_LENGTH,
     DEFAULT_SPARSITY,
     EXPORTS,
     F32,
     LIB_PATH,
     MAX_SEGMENTS,
     MIN_ACTIVE_HEADS,
+    NOTE_NO_LAYOUT,
+    NOTE_NONE,
     SEG_KINDS,
+    STAGE_SPARSE,
+    Stage,
     BlockMask,
     BsattnError,
     Layout,

@@ -59,7 +59,28 @@ class _BlockMask(ctypes.Structure):
 
 EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
-           "bsattn_forward_masked", "bsattn_head_mask", "bsattn_mask_density"]
+           "bsattn_forward_masked", "bsattn_head_mask", "bsattn_mask_density",
+           "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
+           "bsattn_stage_outcome_string"]
+
+class _StageConfig(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("min_length", ctypes.c_int64), ("n_steps", ctypes.c_int32),
+                ("budget_first", ctypes.c_double), ("budget_later", ctypes.c_double),
+                ("switch_step", ctypes.c_int32), ("exclude", ctypes.c_char_p),
+                ("backend_block_mask", ctypes.c_int32), ("backend_masked_block", ctypes.c_int32)]
+
+
+class _StageCall(ctypes.Structure):
+    _fields_ = [("architecture", ctypes.c_char_p), ("pipeline", ctypes.c_char_p), ("denoiser", ctypes.c_char_p),
+                ("self_attention", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+                ("has_token_mask", ctypes.c_int32), ("causal", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("has_layout", ctypes.c_int32)]
+
+
+class _StageDecision(ctypes.Structure):
+    _fields_ = [("outcome", ctypes.c_int32), ("note", ctypes.c_int32), ("budget", ctypes.c_double),
+                ("use_key_mask", ctypes.c_int32), ("first_report", ctypes.c_int32)]
+
 
 _lib = None
 
@@ -95,9 +116,15 @@ def load_library(path: str = LIB_PATH):
                                           ctypes.c_float, ctypes.POINTER(_Tensor), P]
     lib.bsattn_head_mask.argtypes = [P, i32, dbl, i32, P]
     lib.bsattn_mask_density.argtypes = [ctypes.POINTER(_BlockMask), P, ctypes.POINTER(dbl)]
+    lib.bsattn_stage_create.argtypes = [ctypes.POINTER(_StageConfig), ctypes.POINTER(P)]
+    lib.bsattn_stage_decide.argtypes = [P, ctypes.POINTER(_StageCall), ctypes.POINTER(_StageDecision)]
+    lib.bsattn_stage_destroy.argtypes = [P]
+    lib.bsattn_stage_outcome_string.argtypes = [i32]
     for name in EXPORTS[1:]:
-        if name != "bsattn_select_workspace_bytes":
+        if name not in ("bsattn_select_workspace_bytes", "bsattn_stage_destroy", "bsattn_stage_outcome_string"):
             getattr(lib, name).restype = ctypes.c_int
+    lib.bsattn_stage_destroy.restype = None
+    lib.bsattn_stage_outcome_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -303,3 +330,56 @@ def budget_k(n_cand: int, budget: float):
     st = load_library().bsattn_budget_k(n_cand, float(budget), ctypes.byref(k), ctypes.byref(d))
     _check(st, "bsattn_budget_k")
     return int(k.value), bool(d.value)
+
+
+# ---- host stage policy -------------------------------------------------------
+
+STAGE_SPARSE, DECLINE_DISABLED, DECLINE_NO_BACKEND, DECLINE_EXCLUDED, DECLINE_NOT_SELF, \
+    DECLINE_SHORT, DECLINE_CAUSAL, DECLINE_TOKEN_MASK = range(8)
+NOTE_NONE, NOTE_NO_LAYOUT = 0, 1
+DEFAULT_MIN_LENGTH = 8192
+
+
+class Stage:
+    """bsattn_stage_*: the sparse stage's per-call decision (host only).
+
+    schedule: one budget, or (budget_first, budget_later, switch_step) for a
+    per-step schedule with two values over n_steps steps.
+    """
+
+    def __init__(self, *, enabled=True, min_length=DEFAULT_MIN_LENGTH, n_steps=1, schedule=0.3,
+                 exclude="", backend_block_mask=True, backend_masked_block=True):
+        if isinstance(schedule, (tuple, list)):
+            first, later, switch = schedule
+        else:
+            first, later, switch = float(schedule), float(schedule), int(n_steps)
+        self._exclude = (exclude or "").encode()
+        cfg = _StageConfig(int(bool(enabled)), int(min_length), int(n_steps), float(first), float(later),
+                           int(switch), self._exclude, int(bool(backend_block_mask)),
+                           int(bool(backend_masked_block)))
+        self._lib = load_library()
+        self._h = ctypes.c_void_p()
+        _check(self._lib.bsattn_stage_create(ctypes.byref(cfg), ctypes.byref(self._h)), "bsattn_stage_create")
+
+    def decide(self, q_len, kv_len=None, *, step=0, self_attention=True, has_token_mask=False,
+               causal=False, has_layout=True, architecture=None, pipeline=None, denoiser=None) -> dict:
+        enc = lambda x: None if x is None else str(x).encode()
+        call = _StageCall(enc(architecture), enc(pipeline), enc(denoiser), int(bool(self_attention)),
+                          int(q_len), int(q_len if kv_len is None else kv_len), int(bool(has_token_mask)),
+                          int(bool(causal)), int(step), int(bool(has_layout)))
+        d = _StageDecision()
+        _check(self._lib.bsattn_stage_decide(self._h, ctypes.byref(call), ctypes.byref(d)), "bsattn_stage_decide")
+        return {"outcome": d.outcome, "note": d.note, "budget": d.budget, "use_key_mask": bool(d.use_key_mask),
+                "first_report": bool(d.first_report),
+                "reason": self._lib.bsattn_stage_outcome_string(d.outcome).decode()}
+
+    def close(self):
+        if self._h:
+            self._lib.bsattn_stage_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libbsattn.so")
-SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip"]
+SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip", "stage.cpp"]
 HEADERS = ["common.h", "internal.h"]
 # Per-source extra flags.  The attention kernel's scores come out of MFMA
 # accumulators and are never NaN for finite inputs; without NaN semantics
@@ -53,7 +53,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     procs = []
     for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -260,6 +260,91 @@ bsattn_status bsattn_head_mask(const double* importance, int32_t H, double spars
  */
 bsattn_status bsattn_mask_density(const bsattn_block_mask* m, void* stream, double* density);
 
+/* ------------------------------------------------------------------------
+ * Host stage policy (SD.Next commit view, modules/attention/sparse: the
+ * stage-gating, budget-schedule, minimum-length, exclusion-list, decline-log
+ * and no-layout paragraphs).  Decides per attention call whether the sparse
+ * stage serves it and at which budget; pure host code, no GPU.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+    BSATTN_STAGE_SPARSE = 0,          /* serve the call with select + forward      */
+    BSATTN_DECLINE_DISABLED = 1,      /* the feature is switched off               */
+    BSATTN_DECLINE_NO_BACKEND = 2,    /* no backend in the chain consumes a block
+                                         mask: attention stays dense (warned)      */
+    BSATTN_DECLINE_EXCLUDED = 3,      /* the model matched the exclusion list      */
+    BSATTN_DECLINE_NOT_SELF = 4,      /* not self attention (role, or query and
+                                         key lengths differ)                       */
+    BSATTN_DECLINE_SHORT = 5,         /* sequence shorter than the minimum length  */
+    BSATTN_DECLINE_CAUSAL = 6,        /* the call carries a causal flag            */
+    BSATTN_DECLINE_TOKEN_MASK = 7     /* a token mask and no backend that composes
+                                         it with a block mask (masked_block)       */
+} bsattn_stage_outcome;
+
+typedef enum {
+    BSATTN_NOTE_NONE = 0,
+    BSATTN_NOTE_NO_LAYOUT = 1         /* served, but no token layout was published:
+                                         the whole sequence is sparsified          */
+} bsattn_stage_note;
+
+#define BSATTN_DEFAULT_MIN_LENGTH 8192   /* the measured dense/sparse crossover    */
+
+typedef struct {
+    int32_t enabled;
+    int64_t min_length;       /* tokens; 0 = no floor; negative values are reserved
+                                 (a derived floor) and rejected                    */
+    int32_t n_steps;          /* length of the per-step budget schedule, >= 1       */
+    double budget_first;      /* budget of steps [0, switch_step)                  */
+    double budget_later;      /* budget of steps >= switch_step (the schedule has at
+                                 most these two distinct values)                   */
+    int32_t switch_step;      /* 0..n_steps; n_steps = one value throughout         */
+    const char* exclude;      /* comma-separated names, matched case-insensitively
+                                 against the architecture, the pipeline class and
+                                 the denoiser class; NULL or "" = none.  Copied.    */
+    int32_t backend_block_mask;   /* an active backend consumes block masks        */
+    int32_t backend_masked_block; /* ... and takes a token mask with the block mask */
+} bsattn_stage_config;
+
+typedef struct {
+    const char* architecture; /* model names (any may be NULL); the exclusion      */
+    const char* pipeline;     /* result is resolved once per distinct triple        */
+    const char* denoiser;
+    int32_t self_attention;   /* the component role is self attention               */
+    int64_t q_len, kv_len;    /* tokens                                             */
+    int32_t has_token_mask;
+    int32_t causal;
+    int32_t step;             /* denoising step, >= 0; steps past n_steps use the
+                                 last value of the schedule                         */
+    int32_t has_layout;       /* the pipeline published a token layout              */
+} bsattn_stage_call;
+
+typedef struct {
+    int32_t outcome;          /* bsattn_stage_outcome                               */
+    int32_t note;             /* bsattn_stage_note                                  */
+    double budget;            /* this step's budget (outcome SPARSE), else 0        */
+    int32_t use_key_mask;     /* pass the call's token mask to bsattn_forward_masked */
+    int32_t first_report;     /* 1 when this (outcome, note, length) is reported for
+                                 the first time by this stage object: the caller
+                                 logs it once, then stays quiet                     */
+} bsattn_stage_decision;
+
+typedef struct bsattn_stage bsattn_stage;   /* opaque host object */
+
+/* Validates the configuration and creates a stage object (host memory, owned
+ * by the caller until bsattn_stage_destroy).  BSATTN_ERR_BUDGET for a budget
+ * outside (0, inf) or NaN, a negative minimum length or a schedule whose
+ * switch step is outside [0, n_steps]; BSATTN_ERR_NULL for NULL pointers. */
+bsattn_status bsattn_stage_create(const bsattn_stage_config* cfg, bsattn_stage** out);
+
+/* Decides one call.  Thread-safe (an internal lock guards the report memory
+ * and the exclusion cache).  BSATTN_ERR_SHAPE for negative lengths or step. */
+bsattn_status bsattn_stage_decide(bsattn_stage* stage, const bsattn_stage_call* call,
+                                  bsattn_stage_decision* out);
+
+void bsattn_stage_destroy(bsattn_stage* stage);
+
+/* Short human-readable reason for an outcome (static storage). */
+const char* bsattn_stage_outcome_string(int32_t outcome);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,11 @@
 #include "common.h"
 #include "internal.h"
 
+// 1: workgroups of the query heads sharing a K/V head are neighbours
+#ifndef BSATTN_GQA_ORDER
+#define BSATTN_GQA_ORDER 1
+#endif
+
 namespace bsattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -125,11 +130,27 @@ void attn_mfma_kernel(AttnArgs a) {
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
+    // work order (b, kv head, query block, query head within the group): the
+    // query heads that share one K/V head run the same query block on
+    // neighbouring workgroups of one XCD, so their K/V tiles meet in its L2
+    // (the XCD-grouped ids keep neighbours together).  With one query head
+    // per K/V head this is the plain (b, h, query block) order.
+#if BSATTN_GQA_ORDER
+    const int32_t rep = a.H / a.Hkv;
+    const int32_t hr = (int32_t)(L % rep);
+    const int64_t rest = L / rep;
+    const int32_t qb = (int32_t)(rest % a.nqb);
+    const int64_t bg = rest / a.nqb;
+    const int32_t kvh = (int32_t)(bg % a.Hkv);
+    const int32_t b = (int32_t)(bg / a.Hkv);
+    const int32_t h = kvh * rep + hr;
+#else
     const int32_t qb = (int32_t)(L % a.nqb);
     const int64_t bh = L / a.nqb;
     const int32_t h = (int32_t)(bh % a.H);
     const int32_t b = (int32_t)(bh / a.H);
     const int32_t kvh = h / (a.H / a.Hkv);
+#endif
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

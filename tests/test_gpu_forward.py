@@ -138,7 +138,7 @@ def _layout_blocks(w, cls):
     return pick
 
 
-@pytest.mark.parametrize("name", ["joint_text_image_bf16", "video_radial_bf16"])
+@pytest.mark.parametrize("name", ["joint_text_image_bf16", "video_radial_bf16", "video_gqa_bf16"])
 def test_forward_large_workload_sampled(cuda, name):
     w = workloads.ALL[name]
     q, k, v = workloads.make_qkv(w)

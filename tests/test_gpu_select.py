@@ -55,7 +55,7 @@ def test_select_small(cuda, case):
     assert bm.k == oracle.budget(int((oracle.classes(list(segs), N, block) == 0).sum()), budget)[0]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "sdxl_bf16", "joint_text_image_bf16", "video_radial_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "sdxl_bf16", "joint_text_image_bf16", "video_radial_bf16", "video_gqa_bf16"])
 def test_select_workload(cuda, name):
     w = workloads.ALL[name]
     q, k, _ = workloads.make_qkv(w)

@@ -79,7 +79,13 @@ STACK = Workload(
     notes="64 layers x 32 heads; 64 global tokens as a leading pinned prefix; "
           "512-token window; per-layer head masks from U(0,1) importance")
 
-ALL = {w.name: w for w in (TINY, SDXL, JOINT, VIDEO, STACK)}
+VIDEO_GQA = Workload(
+    name="video_gqa_bf16", B=1, H=24, N=33280, D=128, block=64, dtype="bf16", budget=0.3,
+    segments=(("text", 128), ("padding", 384), ("video", 32768)),
+    grid=(8, 64, 64), Hkv=6,
+    notes="the video length with grouped K/V heads (4 query heads per K/V head)")
+
+ALL = {w.name: w for w in (TINY, SDXL, JOINT, VIDEO, STACK, VIDEO_GQA)}
 
 
 def _sparse_span(w: Workload):

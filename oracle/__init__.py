@@ -45,7 +45,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         build()
     lib = ctypes.CDLL(LIB)
     i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
@@ -63,6 +63,14 @@ def _load():
     lib.orc_attention_rows.restype = ctypes.c_int
     lib.orc_head_mask.argtypes = [p, i64, dbl, i64, p]
     lib.orc_head_mask.restype = ctypes.c_int
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = dbl
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e4m3_decode_array.argtypes = [p, i64, p]
+    lib.orc_e4m3_decode_array.restype = None
+    lib.orc_quantize_e4m3.argtypes = [p, i64, i64, i64, i64, p, p]
+    lib.orc_quantize_e4m3.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -184,3 +192,33 @@ def head_mask(importance, sparsity: float = 0.5, min_active: int = 4) -> np.ndar
     out = np.zeros(imp.shape[0], dtype=np.uint8)
     _load().orc_head_mask(_ptr(imp), imp.shape[0], float(sparsity), int(min_active), _ptr(out))
     return out
+
+
+# ---- 8-bit float E4M3 (quantized consumer) --------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of E4M3 codes (uint8 array) as float64; NaN for the NaN codes."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().orc_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code of a float32 value, ties to the even code."""
+    return int(_load().orc_e4m3_encode(float(np.float32(x))))
+
+
+def quantize_e4m3(x):
+    """Per-(b, head) quantisation of x [B,H,N,D] -> (codes uint8 [B,H,N,D], scale float32 [B,H])."""
+    x = _f64(x)
+    B, H, N, D = x.shape
+    codes = np.empty((B, H, N, D), dtype=np.uint8)
+    scale = np.empty((B, H), dtype=np.float32)
+    _load().orc_quantize_e4m3(_ptr(x), B, H, N, D, _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def dequantize_e4m3(codes, scale) -> np.ndarray:
+    """codes [B,H,N,D] times their (b, head) scale, in float64."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, :, None, None]

@@ -371,6 +371,69 @@ int orc_head_mask(const double* importance, int64_t H, double sparsity,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* 8-bit float E4M3 for the quantized consumer [SDN stage paragraph: a      */
+/* quantized kernel joins as a block-mask consumer].  The pages name no     */
+/* format; the reading taken is the OCP E4M3 encoding: sign bit, 4 exponent */
+/* bits with bias 7, 3 mantissa bits; exponent field 0 holds subnormals     */
+/* m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; there is no infinity,    */
+/* the largest finite value is 448.                                         */
+/* ------------------------------------------------------------------------ */
+double orc_e4m3_decode(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest finite E4M3 value to x (a float, compared exactly in double);    */
+/* halfway cases go to the even code (mantissa bit 0 clear).  |x| > 448     */
+/* saturates to 448.  The sign of x is kept (so -0 and tiny negatives give   */
+/* the negative zero code 0x80).                                            */
+uint8_t orc_e4m3_encode(float x)
+{
+    const double ax = fabs((double)x);
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c <= 0x7e; ++c) {           /* every non-negative finite code */
+        const double d = fabs(orc_e4m3_decode((uint8_t)c) - ax);
+        if (d < bestd || (d == bestd && (c & 1) == 0)) { best = c; bestd = d; }
+    }
+    return (uint8_t)(sign | best);
+}
+
+void orc_e4m3_decode_array(const uint8_t* c, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
+}
+
+/* Per-(b, head) quantisation of x [B][H][N][D] (exact bf16 values given in */
+/* double): scale = max|x| / 448 in float (1 when the head is all zero),    */
+/* code = encode(clamp(x / scale, -448, 448)) with the division in float.   */
+int orc_quantize_e4m3(const double* x, int64_t B, int64_t H, int64_t N, int64_t D,
+                      uint8_t* out, float* scale)
+{
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double* xh = x + bh * N * D;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < N * D; ++i) {
+            const float a = fabsf((float)xh[i]);
+            if (a > amax) amax = a;
+        }
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scale[bh] = sc;
+        for (int64_t i = 0; i < N * D; ++i) {
+            float v = (float)xh[i] / sc;
+            if (v > 448.0f) v = 448.0f;
+            if (v < -448.0f) v = -448.0f;
+            out[bh * N * D + i] = orc_e4m3_encode(v);
+        }
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops above use (reported with CPU timings). */
 #ifdef _OPENMP
 #include <omp.h>

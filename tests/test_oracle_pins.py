@@ -494,3 +494,57 @@ def test_padding_contents_do_not_reach_live_rows():
     live = np.r_[0:64, 128:640]
     assert np.array_equal(out[:, :, live], out2[:, :, live])
     assert np.all(out2[:, :, 64:128] == 0)
+
+
+# --------------------------------------------------------------------------
+# 8-bit float E4M3 (quantized consumer).  The pages name no format; the facts
+# pinned here are those of the OCP E4M3 encoding the oracle states it follows:
+# bias 7, 3 mantissa bits, subnormals below 2^-6, one NaN pattern per sign,
+# largest finite 448, round to nearest with ties to even.
+# --------------------------------------------------------------------------
+
+def test_e4m3_decode_known_values():
+    d = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert d[0x38] == 1.0 and d[0x7E] == 448.0 and d[0xFE] == -448.0
+    assert d[0x01] == 2.0 ** -9 and d[0x07] == 7 * 2.0 ** -9 and d[0x08] == 2.0 ** -6
+    assert d[0x40] == 2.0 and d[0x44] == 3.0 and d[0x48] == 4.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.isnan(d).sum() == 2
+    assert d[0x00] == 0.0 and d[0x80] == 0.0 and np.signbit(d[0x80])
+    pos = d[:0x7F]
+    assert np.all(np.diff(pos) > 0)                       # strictly increasing magnitudes
+    assert np.array_equal(d[0x80:0xFF], -d[0x00:0x7F])    # sign symmetry
+
+
+def test_e4m3_encode_round_trip_and_ties_to_even():
+    d = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for c in list(range(0x00, 0x7F)) + list(range(0x81, 0xFF)):
+        assert oracle.e4m3_encode(d[c]) == c
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    for c in range(0x00, 0x7E):
+        lo, hi = d[c], d[c + 1]
+        mid = (lo + hi) / 2
+        assert oracle.e4m3_encode(mid) == (c if c % 2 == 0 else c + 1)     # halfway: even code
+        assert oracle.e4m3_encode(np.nextafter(np.float32(mid), np.float32(0))) == c
+        assert oracle.e4m3_encode(np.nextafter(np.float32(mid), np.float32(1e9))) == c + 1
+    assert oracle.e4m3_encode(1000.0) == 0x7E and oracle.e4m3_encode(-1000.0) == 0xFE
+
+
+def test_e4m3_quantize_scale_and_error_bound():
+    x = rnd((2, 3, 64, 16), 60).astype(np.float32).astype(np.float64)
+    x[1, 2] = 0.0                                          # an all-zero head
+    codes, scale = oracle.quantize_e4m3(x)
+    assert scale[1, 2] == 1.0 and np.all(codes[1, 2] == 0)
+    deq = oracle.dequantize_e4m3(codes, scale)
+    for b in range(2):
+        for h in range(3):
+            if b == 1 and h == 2:
+                continue
+            i = np.unravel_index(np.abs(x[b, h]).argmax(), x[b, h].shape)
+            assert codes[b, h][i] in (0x7E, 0xFE)          # the largest magnitude maps to 448
+            assert scale[b, h] == np.float32(np.float32(np.abs(x[b, h]).max()) / np.float32(448))
+            # round to nearest: within half a step of the neighbouring codes
+            s = float(scale[b, h])
+            err = np.abs(deq[b, h] - x[b, h]) / s
+            mag = np.abs(x[b, h]) / s
+            step = np.where(mag < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3))
+            assert np.all(err <= step / 2 * (1 + 1e-6) + 1e-12)

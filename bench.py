@@ -33,6 +33,7 @@ import head_masked_attention_amd as hm  # noqa: E402
 import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 ATTN_SOURCES = ["head_masked_attention_amd/csrc/attn_mfma.hip", "head_masked_attention_amd/csrc/common.h",
                 "head_masked_attention_amd/csrc/internal.h"]
@@ -356,6 +357,27 @@ def main():
         "note": "bsattn_forward_masked on the step's block mask; tail = last N/16 keys of each batch masked",
     }
 
+    # the fp8 (E4M3) consumer on the step's block mask: per-head quantisation
+    # of Q, K, V (reported separately, a producer-side cost) and the fp8
+    # attention, against the fp8 MFMA peak
+    fp8 = None
+    if w.dtype == "bf16" and w.block == 64 and w.D in (64, 128):
+        q8, qs = hm.quantize_fp8(ly0["qd"])
+        k8, ks = hm.quantize_fp8(ly0["kd"])
+        v8, vs = hm.quantize_fp8(ly0["vd"])
+        out8 = torch.empty_like(outs[0])
+        quant_ms = timer.warm(lambda st: hm.quantize_fp8(ly0["qd"], out=q8, scale=qs, stream=st), reps, args.warmup)
+        fp8_ms = timer.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bms[0], ly0["hmd"], out=out8, stream=st),
+                            reps, args.warmup)
+        fp8_dense_ms = timer.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm_full, ly0["hmd"], out=out8,
+                                                            stream=st), reps, args.warmup)
+        fp8_tf = flops0 / (fp8_ms * 1e-3) / 1e12
+        fp8 = {"attention_ms": fp8_ms, "achieved": fp8_tf, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": fp8_tf / MFMA_FP8_PEAK_TFLOPS, "dense_attention_ms": fp8_dense_ms,
+               "speedup_vs_dense": fp8_dense_ms / fp8_ms, "quantize_one_tensor_ms": quant_ms,
+               "note": "bsattn_forward_fp8 on E4M3 Q/K/V with per-head scales (bf16 out); quantisation of one "
+                       "[B,H,N,D] tensor timed separately"}
+
     cpu = None
     if not args.no_cpu_baseline:
         sample_ids = [0] if not stack else [0, w.layers // 3, 2 * w.layers // 3, w.layers - 1]
@@ -407,6 +429,7 @@ def main():
         "cold": cold,
         "radial": radial,
         "key_mask": key_mask,
+        "fp8": fp8,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "host": platform.node()},

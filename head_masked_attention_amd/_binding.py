@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libbsattn.so")
 DEFAULT_SPARSITY = 0.5
 MIN_ACTIVE_HEADS = 4
 
-BF16, F32 = 0, 1
+BF16, F32, FP8_E4M3 = 0, 1, 2
 SEG_KINDS = {"text": 0, "conditioning": 1, "audio": 2, "other": 3,
              "image": 4, "video": 5, "padding": 6}
 MAX_SEGMENTS = 32
@@ -59,7 +59,8 @@ class _BlockMask(ctypes.Structure):
 
 EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
-           "bsattn_forward_masked", "bsattn_head_mask", "bsattn_mask_density",
+           "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8",
+           "bsattn_head_mask", "bsattn_mask_density",
            "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
            "bsattn_stage_outcome_string"]
 
@@ -114,6 +115,10 @@ def load_library(path: str = LIB_PATH):
     lib.bsattn_forward_masked.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                           ctypes.POINTER(_Tensor), ctypes.POINTER(_BlockMask), P, P, i64,
                                           ctypes.c_float, ctypes.POINTER(_Tensor), P]
+    lib.bsattn_quantize_fp8.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), P, P, ctypes.c_size_t, P]
+    lib.bsattn_forward_fp8.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                       P, P, P, ctypes.POINTER(_BlockMask), P, ctypes.c_float,
+                                       ctypes.POINTER(_Tensor), P]
     lib.bsattn_head_mask.argtypes = [P, i32, dbl, i32, P]
     lib.bsattn_mask_density.argtypes = [ctypes.POINTER(_BlockMask), P, ctypes.POINTER(dbl)]
     lib.bsattn_stage_create.argtypes = [ctypes.POINTER(_StageConfig), ctypes.POINTER(P)]
@@ -176,6 +181,8 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):    # E4M3 codes
+        return FP8_E4M3
     raise BsattnError(2, "tensor", f"unsupported dtype {t.dtype}")
 
 
@@ -284,6 +291,49 @@ def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale:
                                    None if bm is None else ctypes.byref(bm), hm, key_mask.data_ptr(),
                                    int(km_sb), float(scale), ctypes.byref(to), _stream(q.device, stream))
     _check(st, "bsattn_forward_masked")
+    return out
+
+
+def quantize_fp8(x, *, out=None, scale=None, workspace=None, stream=None):
+    """bsattn_quantize_fp8: bf16 [B,H,N,D] -> (E4M3 codes uint8 [B,H,N,D], scale float32 [B,H])."""
+    import torch
+    lib = load_library()
+    B, H = x.shape[0], x.shape[1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(B * H, dtype=torch.int32, device=x.device)
+    tx, to = _tensor(x), _tensor(out)
+    st = lib.bsattn_quantize_fp8(ctypes.byref(tx), ctypes.byref(to), scale.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(x.device, stream))
+    _check(st, "bsattn_quantize_fp8")
+    return out, scale
+
+
+def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_mask: BlockMask | None = None, head_mask=None,
+                scale: float = 0.0, *, out=None, stream=None):
+    """bsattn_forward_fp8: attention on E4M3 inputs with per-(b, head) scales; bf16 output."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    for name, sc, heads in (("q_scale", q_scale, q8.shape[1]), ("k_scale", k_scale, k8.shape[1]),
+                            ("v_scale", v_scale, v8.shape[1])):
+        if sc.dtype != torch.float32 or not sc.is_cuda or not sc.is_contiguous() or sc.numel() != q8.shape[0] * heads:
+            raise BsattnError(3, "bsattn_forward_fp8", f"{name} must be a contiguous float32 device [B, heads]")
+    hm = None
+    if head_mask is not None:
+        if head_mask.dtype != torch.uint8 or not head_mask.is_cuda or head_mask.numel() != q8.shape[1]:
+            raise BsattnError(3, "bsattn_forward_fp8", "head_mask must hold one byte per query head")
+        hm = head_mask.data_ptr()
+    tq, tk, tv, to = _tensor(q8), _tensor(k8), _tensor(v8), _tensor(out)
+    bm = None if block_mask is None else block_mask._c()
+    st = lib.bsattn_forward_fp8(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q_scale.data_ptr(),
+                                k_scale.data_ptr(), v_scale.data_ptr(), None if bm is None else ctypes.byref(bm),
+                                hm, float(scale), ctypes.byref(to), _stream(q8.device, stream))
+    _check(st, "bsattn_forward_fp8")
     return out
 
 

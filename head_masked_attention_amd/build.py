@@ -16,13 +16,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libbsattn.so")
-SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip", "stage.cpp"]
+SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip", "attn_fp8.hip", "stage.cpp"]
 HEADERS = ["common.h", "internal.h"]
 # Per-source extra flags.  The attention kernel's scores come out of MFMA
 # accumulators and are never NaN for finite inputs; without NaN semantics
 # fmaxf lowers to bare v_max / v_max3 instead of also quieting each input
 # first.  (NaN in Q, K or V gives unspecified output.)
-EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"], "attn_fp8.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

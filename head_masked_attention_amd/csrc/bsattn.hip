@@ -17,14 +17,15 @@ using namespace bsattn;
 
 namespace {
 
-size_t elem_size(int32_t dtype) { return dtype == BSATTN_F32 ? 4 : 2; }
+size_t elem_size(int32_t dtype) { return dtype == BSATTN_F32 ? 4 : dtype == BSATTN_FP8_E4M3 ? 1 : 2; }
 
 bool dtype_ok(int32_t dtype) { return dtype == BSATTN_BF16 || dtype == BSATTN_F32; }
 
 // A [B][H][N][D] view: D contiguous, supported D, 16-byte aligned rows.
-bsattn_status check_tensor(const bsattn_tensor* t) {
+// fp8: accept only FP8_E4M3 (the fp8 entry points), else bf16 / fp32.
+bsattn_status check_tensor(const bsattn_tensor* t, bool fp8 = false) {
     if (t == nullptr || t->data == nullptr) return BSATTN_ERR_NULL;
-    if (!dtype_ok(t->dtype)) return BSATTN_ERR_DTYPE;
+    if (fp8 ? t->dtype != BSATTN_FP8_E4M3 : !dtype_ok(t->dtype)) return BSATTN_ERR_DTYPE;
     if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->D <= 0) return BSATTN_ERR_SHAPE;
     if (t->D != 32 && t->D != 64 && t->D != 128) return BSATTN_ERR_SHAPE;
     if (t->B > INT32_MAX || t->H > INT32_MAX || t->N > INT32_MAX) return BSATTN_ERR_SHAPE;
@@ -229,6 +230,73 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
         if (e == hipSuccess)
             e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, s);
     }
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_quantize_fp8(const bsattn_tensor* x, bsattn_tensor* out, float* scale, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    bsattn_status st;
+    if ((st = check_tensor(x)) != BSATTN_OK) return st;
+    if ((st = check_tensor(out, true)) != BSATTN_OK) return st;
+    if (x->dtype != BSATTN_BF16) return BSATTN_ERR_DTYPE;
+    if (out->B != x->B || out->H != x->H || out->N != x->N || out->D != x->D) return BSATTN_ERR_SHAPE;
+    if (scale == nullptr || ws == nullptr) return BSATTN_ERR_NULL;
+    if (ws_bytes < (size_t)(x->B * x->H) * 4 || ((uintptr_t)ws) % 4 != 0 || ((uintptr_t)scale) % 4 != 0)
+        return BSATTN_ERR_WORKSPACE;
+    if (x->B * x->H > INT32_MAX / 2) return BSATTN_ERR_SHAPE;
+    const hipError_t e = launch_quant_fp8(view_of(x), view_of(out), (int)x->B, (int)x->H, x->N, (int)x->D,
+                                          (uint32_t*)ws, scale, (hipStream_t)stream);
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_tensor* v,
+                                 const float* q_scale, const float* k_scale, const float* v_scale,
+                                 const bsattn_block_mask* mask, const uint8_t* head_mask, float scale,
+                                 bsattn_tensor* out, void* stream) {
+    bsattn_status st;
+    if ((st = check_tensor(q, true)) != BSATTN_OK) return st;
+    if ((st = check_tensor(k, true)) != BSATTN_OK) return st;
+    if ((st = check_tensor(v, true)) != BSATTN_OK) return st;
+    if ((st = check_tensor(out)) != BSATTN_OK) return st;
+    if (out->dtype != BSATTN_BF16) return BSATTN_ERR_DTYPE;
+    if (q_scale == nullptr || k_scale == nullptr || v_scale == nullptr) return BSATTN_ERR_NULL;
+    if (k->B != q->B || v->B != q->B || out->B != q->B) return BSATTN_ERR_SHAPE;
+    if (k->N != q->N || v->N != q->N || out->N != q->N) return BSATTN_ERR_SHAPE;
+    if (k->D != q->D || v->D != q->D || out->D != q->D) return BSATTN_ERR_SHAPE;
+    if (v->H != k->H || out->H != q->H || q->H % k->H != 0) return BSATTN_ERR_SHAPE;
+    if (q->D != 64 && q->D != 128) return BSATTN_ERR_UNSUPPORTED;
+    const int64_t block = 64;
+    if (q->N % block != 0) return BSATTN_ERR_SHAPE;
+    if (mask != nullptr) {
+        if (mask->count == nullptr || mask->index == nullptr) return BSATTN_ERR_NULL;
+        if (mask->nqb != q->N / block || mask->nkb != mask->nqb) return BSATTN_ERR_SHAPE;
+        if (!(mask->B == 1 || mask->B == q->B) || !(mask->H == 1 || mask->H == q->H)) return BSATTN_ERR_SHAPE;
+    }
+    if (!std::isfinite(scale)) return BSATTN_ERR_BUDGET;
+    if (k->stride_n > (1 << 24) || v->stride_n > (1 << 24)) return BSATTN_ERR_UNSUPPORTED;
+    AttnArgs a;
+    a.q = view_of(q);
+    a.k = view_of(k);
+    a.v = view_of(v);
+    a.o = out->data;
+    a.o_sb = out->stride_b;
+    a.o_sh = out->stride_h;
+    a.o_sn = out->stride_n;
+    a.B = (int32_t)q->B;
+    a.H = (int32_t)q->H;
+    a.Hkv = (int32_t)k->H;
+    a.nqb = (int32_t)(q->N / block);
+    a.nkb = a.nqb;
+    a.mB = mask ? mask->B : 1;
+    a.mH = mask ? mask->H : 1;
+    a.count = mask ? mask->count : nullptr;
+    a.index = mask ? mask->index : nullptr;
+    a.head_mask = head_mask;
+    a.key_mask = nullptr;
+    a.km_sb = 0;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    a.n_work = (int64_t)a.B * a.H * a.nqb;
+    const hipError_t e = launch_attn_fp8(a, (int)q->D, q_scale, k_scale, v_scale, (hipStream_t)stream);
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
 

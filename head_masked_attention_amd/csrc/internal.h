@@ -29,6 +29,12 @@ hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStr
 
 // bf16, block 64, D in {64, 128}: MFMA path.
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s);
+// fp8 (e4m3) q/k/v with per-(b, head) scales, block 64, D in {64, 128}; bf16 out.
+hipError_t launch_attn_fp8(const AttnArgs& a, int D, const float* q_scale, const float* k_scale,
+                           const float* v_scale, hipStream_t s);
+// bf16 [B][H][N][D] -> e4m3 codes + per-(b, head) scale; amax: B*H words of scratch.
+hipError_t launch_quant_fp8(TView x, TView y, int B, int H, int64_t N, int D, uint32_t* amax, float* scale,
+                            hipStream_t s);
 // any supported dtype / block / D: fp32 vector path.
 hipError_t launch_attn_vec(const AttnArgs& a, int dtype_is_f32, int D, int block, hipStream_t s);
 

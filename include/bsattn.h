@@ -55,8 +55,10 @@ typedef enum {
     BSATTN_ERR_UNSUPPORTED = 9  /* valid request this build has no kernel for          */
 } bsattn_status;
 
-/* Element types of q, k, v and out. */
-typedef enum { BSATTN_BF16 = 0, BSATTN_F32 = 1 } bsattn_dtype;
+/* Element types of q, k, v and out.  FP8_E4M3 (OCP e4m3: 1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, max 448, no infinities) is accepted only
+ * by bsattn_quantize_fp8 (output) and bsattn_forward_fp8 (inputs). */
+typedef enum { BSATTN_BF16 = 0, BSATTN_F32 = 1, BSATTN_FP8_E4M3 = 2 } bsattn_dtype;
 
 /*
  * A device tensor viewed as [B][H][N][D].  Strides are in elements; the D
@@ -241,6 +243,33 @@ bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor*
                                     const uint8_t* head_mask, const uint8_t* key_mask,
                                     int64_t key_mask_stride_b, float scale,
                                     bsattn_tensor* out, void* stream);
+
+/*
+ * fp8 quantisation for the quantized consumer (SD.Next stage paragraph: a
+ * quantized kernel joins as a block-mask consumer).  x: bf16 [B][H][N][D];
+ * out: FP8_E4M3 with the same B, H, N, D (its own strides, in bytes).  Per
+ * (b, h): scale[b * H + h] = max|x| / 448 (1 when the head is all zero), and
+ * out = e4m3(clamp(x / scale, -448, 448)), rounded to nearest even, with the
+ * division in fp32.  scale: device float[B * H]; ws: device scratch of at
+ * least B * H * 4 bytes, 4-byte aligned.  Enqueues three kernels; never
+ * synchronises.
+ */
+bsattn_status bsattn_quantize_fp8(const bsattn_tensor* x, bsattn_tensor* out, float* scale, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention on fp8 inputs (the quantized consumer).
+ *  q [B][H][N][D], k, v [B][Hkv][N][D] of dtype FP8_E4M3 with real values
+ *  code * q_scale[b * H + h] (k_scale, v_scale: [b * Hkv + kv head]; device
+ *  float arrays); out bf16 [B][H][N][D].  Same block mask, head mask and
+ *  scale rules as bsattn_forward (block 64, D 64 or 128).  P is rounded to
+ *  e4m3 for the P V product, and the softmax denominators sum the same
+ *  rounded values.  Enqueues one kernel; never synchronises.
+ */
+bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_tensor* v,
+                                 const float* q_scale, const float* k_scale, const float* v_scale,
+                                 const bsattn_block_mask* mask, const uint8_t* head_mask, float scale,
+                                 bsattn_tensor* out, void* stream);
 
 /*
  * Per-layer head mask (haagenti_sparse AttentionMask / MaskBuilder with

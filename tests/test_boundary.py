@@ -20,7 +20,7 @@ FAKE = 0x7f0000100000            # 16-byte aligned, never dereferenced
 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "bsattn.h")).read()
-    return sorted(set(re.findall(r"\b(bsattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bsattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -203,6 +203,23 @@ def test_forward_masked_validation(lib):
     assert call(FAKE, -256) == 4
     assert call(FAKE, 256, q=tensor(data=0)) == 1      # tensor checks come first
     assert call(FAKE, 0, out=tensor(dtype=B_.F32)) == 2
+
+
+def test_fp8_entry_points_validation(lib):
+    f8 = lambda **kw: tensor(dtype=B_.FP8_E4M3, **kw)
+    m = bmask()
+    fwd8 = lambda q, k, v, out, scales=(FAKE, FAKE, FAKE): lib.bsattn_forward_fp8(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), scales[0], scales[1], scales[2], ctypes.byref(m),
+        None, 0.0, ctypes.byref(out), None)
+    assert fwd8(tensor(), f8(), f8(), tensor()) == 2              # bf16 q
+    assert fwd8(f8(), f8(), f8(), tensor(dtype=B_.F32)) == 2     # out must be bf16
+    assert fwd8(f8(), f8(), f8(), tensor(), scales=(None, FAKE, FAKE)) == 1
+    assert fwd8(f8(D=32), f8(D=32), f8(D=32), tensor(D=32)) == 9  # no kernel for D = 32
+    # the bf16/fp32 entry points refuse E4M3 codes
+    assert call_forward(lib, f8(), f8(), f8(), m, tensor()) == 2
+    x, y = tensor(), f8()
+    assert lib.bsattn_quantize_fp8(ctypes.byref(x), ctypes.byref(y), FAKE, FAKE, 3, None) == 7   # scratch too small
+    assert lib.bsattn_quantize_fp8(ctypes.byref(y), ctypes.byref(y), FAKE, FAKE, 64, None) == 2
 
 
 def test_radial_and_density_validation(lib):

@@ -378,6 +378,16 @@ def main():
                "note": "bsattn_forward_fp8 on E4M3 Q/K/V with per-head scales (bf16 out); quantisation of one "
                        "[B,H,N,D] tensor timed separately"}
 
+    # head masking: the same forward with every head active, for the share of
+    # attention time the layer's head mask skips (the pages claim 50-70 %)
+    head_masking = None
+    if ly0["hmd"] is not None:
+        all_heads = torch.ones(w.H, dtype=torch.uint8, device=dev)
+        t_all = timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], all_heads, out=outs[0],
+                                                 stream=st), reps, args.warmup)
+        head_masking = {"active_heads": int(ly0["hm_np"].sum()), "heads": w.H, "all_heads_ms": t_all,
+                        "masked_ms": fwd_ms, "time_skipped": 1.0 - fwd_ms / t_all}
+
     cpu = None
     if not args.no_cpu_baseline:
         sample_ids = [0] if not stack else [0, w.layers // 3, 2 * w.layers // 3, w.layers - 1]
@@ -430,6 +440,13 @@ def main():
         "radial": radial,
         "key_mask": key_mask,
         "fp8": fp8,
+        "head_masking": head_masking,
+        "pages_context": {
+            "note": "figures printed by the SD.Next commit page and the haagenti_sparse pages, on unstated "
+                    "hardware and precision: context, not targets",
+            "dense_attention_sdxl_ms": 1.2, "selection_overhead_sdxl_ms_before_after": [1.84, 0.23],
+            "budget_30pct_vs_dense_before_after": [0.36, 1.19], "head_masking_compute_skipped_claim": [0.5, 0.7],
+        },
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "host": platform.node()},

@@ -84,22 +84,30 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
     __shared__ __attribute__((aligned(16))) uint8_t V1[TILE];
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (L >= a.n_work) return;
-    // (b, K/V head, query block, query head within the group) order
-    const int32_t rep = a.H / a.Hkv;
-    const int32_t hr = (int32_t)(L % rep);
-    const int64_t rest = L / rep;
-    const int32_t qb = (int32_t)(rest % a.nqb);
-    const int64_t bg = rest / a.nqb;
-    const int32_t kvh = (int32_t)(bg % a.Hkv);
-    const int32_t b = (int32_t)(bg / a.Hkv);
-    const int32_t h = kvh * rep + hr;
+    if (a.head_mask == nullptr && L >= a.n_work) return;
+    // (b, K/V head, query block, query head within the group) order, or
+    // under a head mask the active heads' query blocks first
+    int32_t qb, h, b;
+    bool active = true;
+    if (a.head_mask != nullptr) {
+        const HeadWork hw = head_masked_order(blockIdx.x, gridDim.x, a.head_mask, a.B, a.H, a.nqb);
+        if (!hw.valid) return;
+        qb = hw.qb, h = hw.h, b = hw.b, active = hw.active;
+    } else {
+        const int32_t rep = a.H / a.Hkv;
+        const int32_t hr = (int32_t)(L % rep);
+        const int64_t rest = L / rep;
+        qb = (int32_t)(rest % a.nqb);
+        const int64_t bg = rest / a.nqb;
+        b = (int32_t)(bg / a.Hkv);
+        h = (int32_t)(bg % a.Hkv) * rep + hr;
+    }
+    const int32_t kvh = h / (a.H / a.Hkv);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5, ql = lane & 31;
 
-    const bool active = (a.head_mask == nullptr) || (a.head_mask[h] != 0);
     int32_t cnt = a.nkb;
     const int32_t* list = nullptr;
     if (a.count != nullptr) {
@@ -374,8 +382,7 @@ hipError_t launch_quant_fp8(TView x, TView y, int B, int H, int64_t N, int D, ui
 
 hipError_t launch_attn_fp8(const AttnArgs& a, int D, const float* qs, const float* ks, const float* vs,
                            hipStream_t s) {
-    const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    const dim3 grid((unsigned)padded);
+    const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128) return launch(attn_fp8_kernel<128, 2>, grid, dim3(128), s, a, qs, ks, vs);
     return launch(attn_fp8_kernel<64, 3>, grid, dim3(128), s, a, qs, ks, vs);
 }

@@ -129,28 +129,37 @@ void attn_mfma_kernel(AttnArgs a) {
     static_assert((TILE * 2) % (D * 2) == 0, "tiles hold whole rows");
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (L >= a.n_work) return;
+    if (a.head_mask == nullptr && L >= a.n_work) return;
     // work order (b, kv head, query block, query head within the group): the
     // query heads that share one K/V head run the same query block on
     // neighbouring workgroups of one XCD, so their K/V tiles meet in its L2
     // (the XCD-grouped ids keep neighbours together).  With one query head
     // per K/V head this is the plain (b, h, query block) order.
+    // Under a head mask the active heads' query blocks come first instead,
+    // so that the work the mask keeps spreads evenly over the XCDs.
+    int32_t qb, h, b;
+    bool active = true;
+    if (a.head_mask != nullptr) {
+        const HeadWork hw = head_masked_order(blockIdx.x, gridDim.x, a.head_mask, a.B, a.H, a.nqb);
+        if (!hw.valid) return;
+        qb = hw.qb, h = hw.h, b = hw.b, active = hw.active;
+    } else {
 #if BSATTN_GQA_ORDER
-    const int32_t rep = a.H / a.Hkv;
-    const int32_t hr = (int32_t)(L % rep);
-    const int64_t rest = L / rep;
-    const int32_t qb = (int32_t)(rest % a.nqb);
-    const int64_t bg = rest / a.nqb;
-    const int32_t kvh = (int32_t)(bg % a.Hkv);
-    const int32_t b = (int32_t)(bg / a.Hkv);
-    const int32_t h = kvh * rep + hr;
+        const int32_t rep = a.H / a.Hkv;
+        const int32_t hr = (int32_t)(L % rep);
+        const int64_t rest = L / rep;
+        qb = (int32_t)(rest % a.nqb);
+        const int64_t bg = rest / a.nqb;
+        b = (int32_t)(bg / a.Hkv);
+        h = (int32_t)(bg % a.Hkv) * rep + hr;
 #else
-    const int32_t qb = (int32_t)(L % a.nqb);
-    const int64_t bh = L / a.nqb;
-    const int32_t h = (int32_t)(bh % a.H);
-    const int32_t b = (int32_t)(bh / a.H);
-    const int32_t kvh = h / (a.H / a.Hkv);
+        qb = (int32_t)(L % a.nqb);
+        const int64_t bh = L / a.nqb;
+        h = (int32_t)(bh % a.H);
+        b = (int32_t)(bh / a.H);
 #endif
+    }
+    const int32_t kvh = h / (a.H / a.Hkv);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,7 +168,6 @@ void attn_mfma_kernel(AttnArgs a) {
     const int gtid = tid & 127;              // thread within the group
     const int hl = lane >> 5, ql = lane & 31;
 
-    const bool active = (a.head_mask == nullptr) || (a.head_mask[h] != 0);
     int32_t cnt = a.nkb;
     const int32_t* list = nullptr;
     if (a.count != nullptr) {
@@ -513,8 +521,7 @@ void attn_mfma_kernel(AttnArgs a) {
 
 template <bool KMASK>
 static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
-    const int64_t padded = ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    const dim3 grid((unsigned)padded);
+    const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128)
         return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, BSATTN_D128_WPE, BSATTN_D128_HOIST,
                                        BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE, KMASK>,

@@ -98,6 +98,64 @@ __device__ __forceinline__ int64_t xcd_logical_id(int64_t w, int64_t padded) {
     return (w % kNumXcd) * per + (w / kNumXcd);
 }
 
+// Work order under a per-layer head mask (one wavefront's view; every
+// wavefront of a workgroup computes the same).  Hardware workgroup w runs on
+// XCD w % 8 as that XCD's (w / 8)-th workgroup.  The active heads' query
+// blocks (A items, in (b, active head, query block) order) and the masked
+// heads' (I items) are each split into eight equal contiguous shares, and XCD
+// x takes its share of active items first, then its share of masked ones:
+// the kept work spreads evenly over the XCDs whatever heads the mask keeps,
+// and one head's query blocks stay neighbours on one XCD.  The grid holds
+// 8 * (ceil(n_work / 8) + 1) workgroups, enough for both shares of every XCD;
+// workgroups past them get valid = false.
+struct HeadWork {
+    int32_t b, h, qb;
+    bool active, valid;
+};
+
+__device__ __forceinline__ HeadWork head_masked_order(int64_t w, int64_t padded, const uint8_t* head_mask,
+                                                      int32_t B, int32_t H, int32_t nqb) {
+    const int lane = threadIdx.x & 63;
+    int32_t n_act = 0;
+    for (int32_t h0 = 0; h0 < H; h0 += 64)
+        n_act += __popcll(__ballot(h0 + lane < H && head_mask[h0 + lane] != 0));
+    const int64_t A = (int64_t)B * n_act * nqb;
+    const int64_t I = (int64_t)B * (H - n_act) * nqb;
+    const int64_t x = w % kNumXcd, s = w / kNumXcd;
+    const int64_t a0 = x * A / kNumXcd, a1 = (x + 1) * A / kNumXcd;
+    const int64_t i0 = x * I / kNumXcd, i1 = (x + 1) * I / kNumXcd;
+    (void)padded;
+    HeadWork hw;
+    hw.valid = true;
+    int64_t item;
+    if (s < a1 - a0) { hw.active = true; item = a0 + s; }
+    else if (s - (a1 - a0) < i1 - i0) { hw.active = false; item = i0 + (s - (a1 - a0)); }
+    else { hw.valid = false; hw.active = false; hw.b = hw.h = hw.qb = 0; return hw; }
+    const int32_t nh = hw.active ? n_act : H - n_act;
+    hw.qb = (int32_t)(item % nqb);
+    const int64_t r = item / nqb;
+    int32_t j = (int32_t)(r % nh);
+    hw.b = (int32_t)(r / nh);
+    hw.h = 0;
+    for (int32_t h0 = 0; h0 < H; h0 += 64) {
+        uint64_t m = __ballot(h0 + lane < H && (head_mask[h0 + lane] != 0) == hw.active);
+        const int32_t c = __popcll(m);
+        if (j < c) {
+            for (int32_t k = 0; k < j; ++k) m &= m - 1;   // drop the j lowest set bits
+            hw.h = h0 + __builtin_ctzll(m);
+            break;
+        }
+        j -= c;
+    }
+    return hw;
+}
+
+// Grid of the attention kernels: n_work workgroups padded to a multiple of
+// the XCD count, plus one more round of eight under a head mask.
+__host__ __forceinline__ int64_t attn_grid(int64_t n_work, bool head_masked) {
+    return ((n_work + kNumXcd - 1) / kNumXcd + (head_masked ? 1 : 0)) * kNumXcd;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

@@ -37,6 +37,7 @@ SMALL = [
     ("bf16_block32_d128", 1, 2, 2, 32 * 70, 128, 32, "bf16", (("image", 32 * 60), ("audio", 320)), 0.2, 0),
     ("n_cand_600_e16", 1, 2, 2, 64 * 600, 64, 64, "bf16", (), 0.3, 0),
     ("n_cand_1100_e32", 1, 1, 1, 64 * 1100, 32, 64, "bf16", (), 0.1, 0),
+    ("n_cand_2048_max", 1, 1, 1, 64 * 2048, 32, 64, "bf16", (), 0.05, 0),   # the largest candidate count
     ("split_candidates", 1, 2, 2, 64 * 40, 64, 64, "bf16",
      (("image", 64 * 10), ("text", 64 * 3), ("video", 64 * 20), ("padding", 64 * 2), ("image", 64 * 5)), 0.3, 200),
 ]

@@ -207,3 +207,53 @@ def test_select_rank_resolution_outside_tie_window(cuda, n, D, negative):
     ref, tie = oracle_select(q, kk, (), 64, budget)
     assert tie.sum() == 0, "the construction must keep every row outside the near-tie window"
     assert compare_masks(bm, ref, tie) == 0
+
+
+def random_layout(rng, block):
+    """A random ordered segment list (every kind, lengths not block-aligned)."""
+    kinds = ["text", "conditioning", "audio", "other", "image", "video", "padding"]
+    segs, total = [], 0
+    for _ in range(int(rng.integers(2, 9))):
+        kind = kinds[int(rng.integers(0, len(kinds)))]
+        n = int(rng.integers(1, 12)) * block + (int(rng.integers(0, block)) if rng.random() < 0.4 else 0)
+        segs.append((kind, n))
+        total += n
+    pad = (-total) % block
+    if pad:
+        segs.append(("padding", pad))
+        total += pad
+    return segs, total
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_random_layouts(cuda, seed):
+    # random packed layouts (segments not block-aligned, every token kind),
+    # budgets and windows: masks bit-exact outside near ties
+    rng = np.random.default_rng(1000 + seed)
+    block = 64 if seed % 3 else 32
+    segs, N = random_layout(rng, block)
+    D = [32, 64, 128][seed % 3]
+    budget = float(rng.choice([0.1, 0.25, 0.3, 0.5, 0.9]))
+    window = int(rng.choice([0, 0, 64, 200, 512]))
+    q, k, _ = workloads.small_case(B=1, H=2, N=N, D=D, block=block, dtype="bf16", seed=2000 + seed)
+    bm = run_select(q.to(cuda), k.to(cuda), segs, block, budget, window)
+    ref, tie = oracle_select(q, k, segs, block, budget, window)
+    compare_masks(bm, ref, tie)
+
+
+def test_select_and_forward_long_sequence(cuda):
+    # 131072 tokens (2048 key blocks) on one head: the largest candidate count
+    # through select and forward, forward checked on sampled rows
+    from parity import upload_mask, assert_close
+    N, D = 64 * 2048, 128
+    q, k, v = workloads.small_case(B=1, H=1, N=N, D=D, seed=2100)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    bm = run_select(qd, kd, (), 64, 0.02)
+    ref, tie = oracle_select(q, k, (), 64, 0.02)
+    compare_masks(bm, ref, tie)
+    out = hm.forward(qd, kd, vd, upload_mask(ref, cuda))
+    torch.cuda.synchronize()
+    rows = np.stack([np.zeros(48, int), np.zeros(48, int), np.random.default_rng(2101).integers(0, N, 48)], 1)
+    refo = oracle.attention(to64(q), to64(k), to64(v), 64, ref, rows=rows)
+    got = out.cpu()[rows[:, 0], rows[:, 1], rows[:, 2]].double().numpy()
+    assert_close(got, refo, "bf16", "long sequence")

@@ -504,7 +504,7 @@ void attn_mfma_kernel(AttnArgs a) {
 #define BSATTN_D64_VSINGLE true
 #endif
 #ifndef BSATTN_D128_VSINGLE
-#define BSATTN_D128_VSINGLE false
+#define BSATTN_D128_VSINGLE true
 #endif
 #ifndef BSATTN_D128_KT
 #define BSATTN_D128_KT 32
@@ -513,17 +513,18 @@ void attn_mfma_kernel(AttnArgs a) {
 #define BSATTN_D128_SPLIT 1
 #endif
 #ifndef BSATTN_D128_WPE
-#define BSATTN_D128_WPE 2
+#define BSATTN_D128_WPE 3
 #endif
 #ifndef BSATTN_D128_HOIST
-#define BSATTN_D128_HOIST true
+#define BSATTN_D128_HOIST false
 #endif
 
 template <bool KMASK>
 static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128)
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, BSATTN_D128_WPE, BSATTN_D128_HOIST,
+        // the masked variant needs more registers: two waves per SIMD
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE, BSATTN_D128_HOIST,
                                        BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
     // the masked variant needs a few more registers: one wave less per SIMD

@@ -99,7 +99,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // with its own LDS stages, and the groups' partial softmax states are merged
 // through LDS at the end.  More wavefronts per query block hide more latency
 // when the grid alone cannot fill the chip.
-template <int D, int KT, int SPLIT, int WPE, bool HOIST, bool LAUNDER, bool VSINGLE, bool KMASK>
+template <int D, int KT, int SPLIT, int WPE, bool VSINGLE, bool KMASK>
 __global__ __launch_bounds__(128 * SPLIT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
@@ -116,7 +116,6 @@ void attn_mfma_kernel(AttnArgs a) {
     static_assert(NI >= 1 && KT * CPR % 128 == 0, "stage tiling");
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
     static_assert(SPLIT == 1 || SPLIT * TILE * 2 >= D * 128, "merge buffer fits in one stage object");
-    static_assert(!(VSINGLE && HOIST), "a single V stage is read only after its own barrier");
     static_assert(!KMASK || KT == 32, "key-mask words cover one 32-key stage");
 
     // one LDS object per stage (holding every group's tile): distinct objects
@@ -308,21 +307,15 @@ void attn_mfma_kernel(AttnArgs a) {
             return;
         }
 
-        // with LAUNDER the offsets pass through an empty asm once per stage, so the
-        // compiler recomputes the XORs here instead of keeping every
-        // fragment address live across the loop
-        uint32_t kbs = kb, vbs0 = vb0, vbs1 = vb1;
-        if constexpr (LAUNDER) asm volatile("" : "+v"(kbs), "+v"(vbs0), "+v"(vbs1));
         const uint8_t* Kb = (const uint8_t*)Kt;
         const uint8_t* Vb = (const uint8_t*)Vt;
 
         // V^T operands of O^T += V^T P^T.  Within each 16-lane group, lane j
         // supplies V[kb + j/4][d0 + 4*(j%4) .. +3]; lane i then receives
-        // V[kb + 0..3][d0 + i].  With HOIST they are read, with the K
-        // fragments, at the top of the stage, so one LDS round trip covers both.
+        // V[kb + 0..3][d0 + i].
         auto v_operand = [&](int dt, int ks) -> bf16x8 {
-            const uint32_t o0 = (vbs0 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
-            const uint32_t o1 = (vbs1 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
+            const uint32_t o0 = (vb0 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
+            const uint32_t o1 = (vb1 ^ (uint32_t)(64 * dt)) + 32 * D * ks;
             const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(Vb + o0));
             const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(Vb + o1));
             const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -333,15 +326,7 @@ void attn_mfma_kernel(AttnArgs a) {
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                kf[kt][ks] = *(const bf16x8*)(Kb + (kbs ^ (uint32_t)(32 * ks)) + 64 * D * kt);
-        bf16x8 vf[HOIST ? NDT : 1][HOIST ? NPS : 1];
-        if constexpr (HOIST) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int ks = 0; ks < NPS; ++ks) vf[dt][ks] = v_operand(dt, ks);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                kf[kt][ks] = *(const bf16x8*)(Kb + (kb ^ (uint32_t)(32 * ks)) + 64 * D * kt);
 
         // S^T for NKT 32-key tiles
         f16v sacc[NKT];
@@ -425,8 +410,7 @@ void attn_mfma_kernel(AttnArgs a) {
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int ks = 0; ks < NPS; ++ks) {
-                const bf16x8 va = HOIST ? vf[HOIST ? dt : 0][HOIST ? ks : 0] : v_operand(dt, ks);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], oacc[dt], 0, 0, 0);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(dt, ks), pf[ks], oacc[dt], 0, 0, 0);
             }
     };
     for (int t = 0; t < T; t += 2) {
@@ -481,7 +465,7 @@ void attn_mfma_kernel(AttnArgs a) {
 }
 
 // Launch shapes per head dim: keys per LDS stage, key-block groups per
-// workgroup, waves per EU, hoisted V reads.  Chosen by measured sweeps.
+// workgroup, waves per EU, single-buffered V.  Chosen by measured sweeps.
 #ifndef BSATTN_D64_KT
 #define BSATTN_D64_KT 32
 #endif
@@ -490,15 +474,6 @@ void attn_mfma_kernel(AttnArgs a) {
 #endif
 #ifndef BSATTN_D64_WPE
 #define BSATTN_D64_WPE 5
-#endif
-#ifndef BSATTN_D64_HOIST
-#define BSATTN_D64_HOIST false
-#endif
-#ifndef BSATTN_D64_LAUNDER
-#define BSATTN_D64_LAUNDER false
-#endif
-#ifndef BSATTN_D128_LAUNDER
-#define BSATTN_D128_LAUNDER false
 #endif
 #ifndef BSATTN_D64_VSINGLE
 #define BSATTN_D64_VSINGLE true
@@ -515,21 +490,18 @@ void attn_mfma_kernel(AttnArgs a) {
 #ifndef BSATTN_D128_WPE
 #define BSATTN_D128_WPE 3
 #endif
-#ifndef BSATTN_D128_HOIST
-#define BSATTN_D128_HOIST false
-#endif
 
 template <bool KMASK>
 static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128)
         // the masked variant needs more registers: two waves per SIMD
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE, BSATTN_D128_HOIST,
-                                       BSATTN_D128_LAUNDER, BSATTN_D128_VSINGLE, KMASK>,
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE,
+                                       BSATTN_D128_VSINGLE, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
     // the masked variant needs a few more registers: one wave less per SIMD
-    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? 4 : BSATTN_D64_WPE, BSATTN_D64_HOIST,
-                                   BSATTN_D64_LAUNDER, BSATTN_D64_VSINGLE, KMASK>,
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? 4 : BSATTN_D64_WPE,
+                                   BSATTN_D64_VSINGLE, KMASK>,
                   grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }
 

@@ -433,3 +433,30 @@ class Stage:
             self.close()
         except Exception:
             pass
+
+
+def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, step: int = 0, head_mask=None,
+                     key_mask=None, causal: bool = False, self_attention: bool = True, architecture=None,
+                     pipeline=None, denoiser=None, out=None, stream=None):
+    """One attention call through the sparse stage (orchestration only).
+
+    Asks the stage whether to serve the call; if it does, runs bsattn_select at
+    the step's budget and bsattn_forward (bsattn_forward_masked when the call
+    carries a token key mask).  A declined self-attention call of a supported
+    shape is computed dense by the same kernel (every block kept); a causal
+    or cross-attention call returns None for the caller's own attention.
+    Returns (out or None, decision).
+    """
+    has_layout = layout is not None and len(layout.segments) > 0
+    d = stage.decide(q.shape[2], k.shape[2], step=step, self_attention=self_attention,
+                     has_token_mask=key_mask is not None, causal=causal, has_layout=has_layout,
+                     architecture=architecture, pipeline=pipeline, denoiser=denoiser)
+    if d["outcome"] == STAGE_SPARSE:
+        lay = layout if layout is not None else Layout(64, [])
+        bm = select(q, k, lay, d["budget"], stream=stream)
+        out = forward(q, k, v, bm, head_mask, out=out, stream=stream,
+                      key_mask=key_mask if d["use_key_mask"] else None)
+        return out, d
+    if d["outcome"] in (DECLINE_CAUSAL, DECLINE_NOT_SELF) or q.shape[2] % 64 != 0:
+        return None, d
+    return forward(q, k, v, None, head_mask, out=out, stream=stream, key_mask=key_mask), d

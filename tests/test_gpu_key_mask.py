@@ -125,3 +125,32 @@ def test_straddling_layout_exact_with_token_mask(cuda):
     out2 = hm.forward(qd, k2.to(cuda), v2.to(cuda), bm, key_mask=torch.from_numpy(km).to(cuda))
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+def test_sparse_attention_through_the_stage(cuda):
+    # the stage serves a long self-attention call (select + forward, with the
+    # token mask), declines a short one (dense through the same kernel) and
+    # hands a causal one back to the caller
+    segs = [("text", 100), ("padding", 60), ("image", 64 * 10 - 160 + 64 * 6)]
+    N = sum(n for _, n in segs)
+    q, k, v = workloads.small_case(B=1, H=2, N=N, D=64, seed=31)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    km = np.ones((1, N), np.uint8)
+    km[:, 100:160] = 0
+    kmd = torch.from_numpy(km).to(cuda)
+    lay = hm.Layout(64, segs)
+    stage = hm.Stage(min_length=512, n_steps=4, schedule=(0.5, 0.25, 2))
+    out, d = hm.sparse_attention(qd, kd, vd, stage, lay, step=3, key_mask=kmd)
+    torch.cuda.synchronize()
+    assert d["outcome"] == hm.STAGE_SPARSE and d["budget"] == 0.25 and d["use_key_mask"]
+    bm = hm.select(qd, kd, lay, 0.25)
+    ref = hm.forward(qd, kd, vd, bm, key_mask=kmd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    short = hm.Stage(min_length=4096)
+    out2, d2 = hm.sparse_attention(qd, kd, vd, short, lay)
+    torch.cuda.synchronize()
+    assert d2["outcome"] == hm.DECLINE_SHORT and d2["first_report"]
+    assert torch.equal(out2, hm.forward(qd, kd, vd))
+    out3, d3 = hm.sparse_attention(qd, kd, vd, stage, lay, causal=True)
+    assert out3 is None and d3["outcome"] == hm.DECLINE_CAUSAL

@@ -6,8 +6,10 @@
 // end.  Each pair walks its share of the compacted list of kept key blocks
 // (CSR-like, ascending) in stages of KT keys:
 //   - K and V stage tiles go from HBM/L2 straight into LDS with
-//     global_load_lds_dwordx4 (no register staging), two stages deep, one
-//     barrier per stage;
+//     global_load_lds_dwordx4 (no register staging): V two stages deep, K
+//     one, and the next K tile loads as soon as every wavefront has read
+//     this stage's K fragments (two barriers per stage, neither of which
+//     waits for tiles still in flight);
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the Q^T fragments held in
 //     VGPRs for the whole loop;
 //   - online softmax in fp32: exp2 with the scale folded into log2 units, and
@@ -35,6 +37,10 @@
 // 1: workgroups of the query heads sharing a K/V head are neighbours
 #ifndef BSATTN_GQA_ORDER
 #define BSATTN_GQA_ORDER 1
+#endif
+// 1: a wavefront's issue priority falls as its workgroup progresses
+#ifndef BSATTN_PRIO
+#define BSATTN_PRIO 1
 #endif
 
 namespace bsattn {
@@ -94,12 +100,29 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for the LDS stages.  __syncthreads() also waits for
+// every vector-memory operation of the wave (vmcnt 0), and the LDS-DMA stage
+// loads count there, so a barrier in mid-stage would wait for the next
+// stage's tiles too.  Here the wave's own LDS reads complete first (the
+// buffer a stage frees may be overwritten once every wave is past the
+// barrier), the compiler may not move memory accesses across it, and the
+// tile loads are waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS stage buffering of the attention kernel: both K and V double-buffered,
+// V single (loaded after a stage's first barrier, waited for before P V), or
+// K single (the next stage's K is loaded once every wavefront holds this
+// stage's K fragments in registers).
+enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
+
 // SPLIT key-block groups per workgroup: group g (wavefronts 2g, 2g + 1)
 // takes the kept blocks at list positions g, g + SPLIT, g + 2 SPLIT, ...
 // with its own LDS stages, and the groups' partial softmax states are merged
 // through LDS at the end.  More wavefronts per query block hide more latency
 // when the grid alone cannot fill the chip.
-template <int D, int KT, int SPLIT, int WPE, bool VSINGLE, bool KMASK>
+template <int D, int KT, int SPLIT, int WPE, int BUF, bool KMASK>
 __global__ __launch_bounds__(128 * SPLIT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
@@ -123,8 +146,8 @@ void attn_mfma_kernel(AttnArgs a) {
     // in flight into the other
     __shared__ __attribute__((aligned(16))) uint16_t K0[SPLIT * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t V0[SPLIT * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t K1[SPLIT * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t V1[VSINGLE ? 8 : SPLIT * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t K1[BUF == BUF_K1 ? 8 : SPLIT * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t V1[BUF == BUF_V1 ? 8 : SPLIT * TILE];
     static_assert((TILE * 2) % (D * 2) == 0, "tiles hold whole rows");
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -169,10 +192,14 @@ void attn_mfma_kernel(AttnArgs a) {
 
     int32_t cnt = a.nkb;
     const int32_t* list = nullptr;
+    int32_t blk0 = grp;                      // the group's first key block
     if (a.count != nullptr) {
         const int64_t ms = (int64_t)(a.mB == 1 ? 0 : b) * a.mH + (a.mH == 1 ? 0 : h);
         cnt = a.count[ms * a.nqb + qb];
         list = a.index + (ms * a.nqb + qb) * (int64_t)a.nkb;
+        // read together with the count rather than after it (an entry of the
+        // row either way; unused when the group has no block)
+        blk0 = ((const __attribute__((address_space(4))) int32_t*)list)[grp < a.nkb ? grp : 0];
     }
     uint16_t* obase = (uint16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qb * BLK * a.o_sn;
 
@@ -204,7 +231,7 @@ void attn_mfma_kernel(AttnArgs a) {
         (const __attribute__((address_space(4))) int32_t*)list;
     auto block_of = [&](int t) -> int32_t {
         const int i = (t / SUB) * SPLIT + grp;
-        return list == nullptr ? i : klist[i];
+        return t < SUB ? blk0 : (list == nullptr ? i : klist[i]);
     };
     // per-thread source offsets of the NI chunks it loads per stage: chunk
     // slot s = i*128 + gtid of the group's tile holds row s / CPR, global
@@ -248,15 +275,21 @@ void attn_mfma_kernel(AttnArgs a) {
             km_next = lane < 32 ? (uint32_t)kmbase[row0 + lane] : 1u;
         }
     };
-    // With VSINGLE the group has one V tile: V of stage t is loaded after the
-    // stage's first barrier (every wave is past the previous P V) and waited
-    // for at a second barrier before this stage's P V, while K stays double
-    // buffered.  This keeps the workgroup's LDS small enough for five
+    // One of K and V may have a single tile per group, which keeps the
+    // workgroup's LDS small enough for five (D = 64) or six (D = 128)
     // workgroups per CU.
+    //  BUF_V1: V of stage t is loaded after the stage's first barrier (every
+    //    wave is past the previous P V) and waited for at a second barrier
+    //    before this stage's P V; K is double-buffered.
+    //  BUF_K1: the K fragments of stage t are read right after the first
+    //    barrier; a second barrier then frees the K tile and K of stage t + 1
+    //    is loaded while stage t computes.  V is double-buffered and loaded a
+    //    stage ahead, so both tiles have about a whole stage to arrive.
     if (Tg > 0) {
+        if constexpr (BUF == BUF_K1) issue_v(0, V0 + grp * TILE);
         issue_m(0);
         issue_k(0, K0 + grp * TILE);
-        if constexpr (!VSINGLE) issue_v(0, V0 + grp * TILE);
+        if constexpr (BUF == BUF_KV2) issue_v(0, V0 + grp * TILE);
     }
 
     // Per-lane byte offsets of this lane's LDS fragments within a stage
@@ -289,26 +322,66 @@ void attn_mfma_kernel(AttnArgs a) {
     // one stage: wait for its tiles, make them visible, start the loads of
     // stage t + 1 into the buffers freed by stage t - 1, then compute
     auto stage = [&](int t, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
+#if BSATTN_PRIO
+        // Issue priority 3, 2, 1, 0 over the four quarters of the workgroup's
+        // stages.  The SIMD arbiter otherwise prefers the oldest wavefront:
+        // the workgroups of one CU, started together with equal work, then
+        // finish one after another and the last ones run at low occupancy.
+        // Favouring the least advanced keeps them abreast.
+        {
+            const int pr = 3 - min(3, (4 * t) / T);
+            if (pr == 3) __builtin_amdgcn_s_setprio(3);
+            else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+            else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
+#endif
         wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         // this stage's key-mask word (wave-uniform); all ones without KMASK
         uint32_t kw = 0xffffffffu;
         if constexpr (KMASK) kw = (uint32_t)__ballot(km_next != 0u);
-        if constexpr (VSINGLE) {
+        if constexpr (BUF == BUF_V1) {
             if (t < Tg) issue_v(t, V0 + grp * TILE);
             if (t + 1 < Tg) { issue_m(t + 1); issue_k(t + 1, Kn); }
+        } else if constexpr (BUF == BUF_K1) {
+            if (t + 1 < Tg) issue_v(t + 1, Vn);
         } else if (t + 1 < Tg) {
             issue_m(t + 1);
             issue_k(t + 1, Kn);
             issue_v(t + 1, Vn);
         }
-        if (t >= Tg || (KMASK && kw == 0u)) {   // no work, or every key of the stage masked
-            if constexpr (VSINGLE) __syncthreads();   // the stage's second barrier
-            return;
-        }
+        // no work: past the group's blocks, or every key of the stage masked
+        const bool work = t < Tg && !(KMASK && kw == 0u);
 
         const uint8_t* Kb = (const uint8_t*)Kt;
         const uint8_t* Vb = (const uint8_t*)Vt;
+        // S^T = K Q^T for NKT 32-key tiles
+        f16v sacc[NKT];
+        if (work) {
+            bf16x8 kf[NKT][NKS];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    kf[kt][ks] = *(const bf16x8*)(Kb + (kb ^ (uint32_t)(32 * ks)) + 64 * D * kt);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][ks], qf[ks], sacc[kt], 0, 0, 0);
+            }
+        }
+        if constexpr (BUF == BUF_K1) {
+            lds_barrier();   // every wave has read its K fragments: the K tile is free
+            if (t + 1 < Tg) { issue_m(t + 1); issue_k(t + 1, Kn); }
+        }
+        if (!work) {
+            if constexpr (BUF == BUF_V1) lds_barrier();   // the stage's second barrier
+            return;
+        }
 
         // V^T operands of O^T += V^T P^T.  Within each 16-lane group, lane j
         // supplies V[kb + j/4][d0 + 4*(j%4) .. +3]; lane i then receives
@@ -321,23 +394,7 @@ void attn_mfma_kernel(AttnArgs a) {
             const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             return __builtin_bit_cast(bf16x8, both);
         };
-        bf16x8 kf[NKT][NKS];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                kf[kt][ks] = *(const bf16x8*)(Kb + (kb ^ (uint32_t)(32 * ks)) + 64 * D * kt);
 
-        // S^T for NKT 32-key tiles
-        f16v sacc[NKT];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][ks], qf[ks], sacc[kt], 0, 0, 0);
-        }
         if constexpr (KMASK) {
             // masked keys of a partly masked stage: -inf scores.  Element r of
             // lane half hl holds key (r & 7) | (hl << 3) | ((r >> 3) << 4).
@@ -398,11 +455,11 @@ void attn_mfma_kernel(AttnArgs a) {
             }
         l_run += psum2[0] + psum2[1];
 
-        if constexpr (VSINGLE) {
+        if constexpr (BUF == BUF_V1) {
             // this stage's V has landed; the next stage's K may still fly
             if (t + 1 < Tg) wait_vmcnt<NI>();
             else wait_vmcnt<0>();
-            __syncthreads();
+            lds_barrier();
         }
 
         // O^T += V^T P^T
@@ -414,8 +471,13 @@ void attn_mfma_kernel(AttnArgs a) {
             }
     };
     for (int t = 0; t < T; t += 2) {
-        stage(t, K0, V0, K1 + grp * TILE, (VSINGLE ? V0 : V1) + grp * TILE);
-        if (t + 1 < T) stage(t + 1, K1, VSINGLE ? V0 : V1, K0 + grp * TILE, V0 + grp * TILE);
+        if constexpr (BUF == BUF_K1) {
+            stage(t, K0, V0, K0 + grp * TILE, V1 + grp * TILE);
+            if (t + 1 < T) stage(t + 1, K0, V1, K0 + grp * TILE, V0 + grp * TILE);
+        } else {
+            stage(t, K0, V0, K1 + grp * TILE, (BUF == BUF_V1 ? V0 : V1) + grp * TILE);
+            if (t + 1 < T) stage(t + 1, K1, BUF == BUF_V1 ? V0 : V1, K0 + grp * TILE, V0 + grp * TILE);
+        }
     }
 
     if constexpr (SPLIT == 2) {
@@ -424,7 +486,7 @@ void attn_mfma_kernel(AttnArgs a) {
         // stage load is in flight here (the last stage waited for all).
         __syncthreads();
         float* po = (float*)(wq == 0 ? K0 : V0);        // [NDT * 16][64 lanes]
-        float* pml = (float*)K1 + wq * 128;              // m [64 lanes], l [64 lanes]
+        float* pml = (float*)(BUF == BUF_K1 ? V1 : K1) + wq * 128;   // m [64 lanes], l [64 lanes]
         if (grp == 1) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
@@ -465,7 +527,7 @@ void attn_mfma_kernel(AttnArgs a) {
 }
 
 // Launch shapes per head dim: keys per LDS stage, key-block groups per
-// workgroup, waves per EU, single-buffered V.  Chosen by measured sweeps.
+// workgroup, waves per EU, stage buffering.  Chosen by measured sweeps.
 #ifndef BSATTN_D64_KT
 #define BSATTN_D64_KT 32
 #endif
@@ -475,11 +537,11 @@ void attn_mfma_kernel(AttnArgs a) {
 #ifndef BSATTN_D64_WPE
 #define BSATTN_D64_WPE 5
 #endif
-#ifndef BSATTN_D64_VSINGLE
-#define BSATTN_D64_VSINGLE true
+#ifndef BSATTN_D64_BUF
+#define BSATTN_D64_BUF BUF_K1
 #endif
-#ifndef BSATTN_D128_VSINGLE
-#define BSATTN_D128_VSINGLE true
+#ifndef BSATTN_D128_BUF
+#define BSATTN_D128_BUF BUF_K1
 #endif
 #ifndef BSATTN_D128_KT
 #define BSATTN_D128_KT 32
@@ -497,11 +559,11 @@ static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     if (D == 128)
         // the masked variant needs more registers: two waves per SIMD
         return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE,
-                                       BSATTN_D128_VSINGLE, KMASK>,
+                                       BSATTN_D128_BUF, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
     // the masked variant needs a few more registers: one wave less per SIMD
     return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? 4 : BSATTN_D64_WPE,
-                                   BSATTN_D64_VSINGLE, KMASK>,
+                                   BSATTN_D64_BUF, KMASK>,
                   grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }
 

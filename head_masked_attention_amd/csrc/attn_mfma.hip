@@ -100,6 +100,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// LDS-DMA of one 16-byte chunk per lane through a buffer resource based at
+// `base` (raw buffer, 32-bit data format; the range only has to cover the
+// stage tile): lane l's chunk at base + off lands at dst + 16 l.  The loads
+// of a tile share the scalar resource, so each is base plus the lane's
+// 32-bit offset with no per-load address arithmetic.
+__device__ __forceinline__ void chunk_to_lds(const uint16_t* base, uint32_t off, uint16_t* dst) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
 // Workgroup barrier for the LDS stages.  __syncthreads() also waits for
 // every vector-memory operation of the wave (vmcnt 0), and the LDS-DMA stage
 // loads count there, so a barrier in mid-stage would wait for the next
@@ -236,34 +246,25 @@ void attn_mfma_kernel(AttnArgs a) {
     // per-thread source offsets of the NI chunks it loads per stage: chunk
     // slot s = i*128 + gtid of the group's tile holds row s / CPR, global
     // chunk (s % CPR) ^ swizzle
-    int32_t koff[NI], voff[NI];
+    // Per-lane byte offsets within a stage tile (the tile's first row is the
+    // buffer base of its loads).
+    uint32_t koff[NI], voff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int s = i * 128 + gtid;
         const int r = s / CPR;
         const int c = (s % CPR) ^ chunk_swizzle<D>(r);
-        koff[i] = r * (int32_t)a.k.sn + c * 8;
-        voff[i] = r * (int32_t)a.v.sn + c * 8;
+        koff[i] = (uint32_t)(r * (int32_t)a.k.sn + c * 8) * 2u;
+        voff[i] = (uint32_t)(r * (int32_t)a.v.sn + c * 8) * 2u;
     }
+    auto issue_tile = [&](const uint16_t* base, int64_t sn, const uint32_t (&off)[NI], int t, uint16_t* dst) {
+        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) chunk_to_lds(base + row0 * sn, off[i], dst + (i * 128 + wq * 64) * 8);
+    };
     // issue the K (or V) loads of stage t into the group's tile at Kd (Vd)
-    auto issue_k = [&](int t, uint16_t* Kd) {
-        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
-        const uint16_t* kt = kbase + row0 * a.k.sn;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(kt + koff[i]),
-                (__attribute__((address_space(3))) void*)(Kd + (i * 128 + wq * 64) * 8), 16, 0, 0);
-    };
-    auto issue_v = [&](int t, uint16_t* Vd) {
-        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
-        const uint16_t* vt = vbase + row0 * a.v.sn;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(vt + voff[i]),
-                (__attribute__((address_space(3))) void*)(Vd + (i * 128 + wq * 64) * 8), 16, 0, 0);
-    };
+    auto issue_k = [&](int t, uint16_t* Kd) { issue_tile(kbase, a.k.sn, koff, t, Kd); };
+    auto issue_v = [&](int t, uint16_t* Vd) { issue_tile(vbase, a.v.sn, voff, t, Vd); };
     // KMASK: lanes 0..31 fetch the mask bytes of the 32 keys of a stage with
     // its K tile (after its V); at the stage a ballot turns them into one
     // wave-uniform 32-bit word.
@@ -537,6 +538,9 @@ void attn_mfma_kernel(AttnArgs a) {
 #ifndef BSATTN_D64_WPE
 #define BSATTN_D64_WPE 5
 #endif
+#ifndef BSATTN_D64_KM_WPE
+#define BSATTN_D64_KM_WPE 4
+#endif
 #ifndef BSATTN_D64_BUF
 #define BSATTN_D64_BUF BUF_K1
 #endif
@@ -561,8 +565,8 @@ static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
         return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE,
                                        BSATTN_D128_BUF, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
-    // the masked variant needs a few more registers: one wave less per SIMD
-    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? 4 : BSATTN_D64_WPE,
+    // the masked variant needs a few more registers
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? BSATTN_D64_KM_WPE : BSATTN_D64_WPE,
                                    BSATTN_D64_BUF, KMASK>,
                   grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }

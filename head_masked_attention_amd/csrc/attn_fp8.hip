@@ -5,7 +5,7 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the output is
 // bf16.  One workgroup of two wavefronts per (b, query block, query head),
 // each wavefront owning 32 query rows; one stage per kept 64-key block, K and
-// V double-buffered in LDS (global_load_lds_dwordx4, 16-byte chunks XOR-
+// V double-buffered in LDS (buffer_load_dwordx4 ... lds, 16-byte chunks XOR-
 // swizzled by row).
 //   - S^T = K Q^T: two 32-key tiles per stage and D / 64 k-steps; the K rows
 //     enter the MFMA row slots in an order that leaves lane half h holding the
@@ -146,14 +146,14 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
     auto block_of = [&](int t) -> int32_t { return list == nullptr ? t : klist[t]; };
     // per-thread source offsets: chunk slot s = i*128 + tid holds row s / CPR,
     // global chunk (s % CPR) ^ swizzle
-    int32_t koff[NI], voff[NI];
+    uint32_t koff[NI], voff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int s = i * 128 + tid;
         const int r = s / CPR;
         const int c = (s % CPR) ^ f8_swizzle<D>(r);
-        koff[i] = r * (int32_t)a.k.sn + c * 16;
-        voff[i] = r * (int32_t)a.v.sn + c * 16;
+        koff[i] = (uint32_t)(r * (int32_t)a.k.sn + c * 16);
+        voff[i] = (uint32_t)(r * (int32_t)a.v.sn + c * 16);
     }
     auto issue = [&](int t, uint8_t* Kd, uint8_t* Vd) {
         const int64_t row0 = (int64_t)block_of(t) * BLK;
@@ -162,10 +162,8 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int dst = (i * 128 + wave * 64) * 16;   // wave-uniform byte offset
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + koff[i]),
-                                             (__attribute__((address_space(3))) void*)(Kd + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + voff[i]),
-                                             (__attribute__((address_space(3))) void*)(Vd + dst), 16, 0, 0);
+            chunk_to_lds(kt, koff[i], Kd + dst);
+            chunk_to_lds(vt, voff[i], Vd + dst);
         }
     };
     issue(0, K0, V0);

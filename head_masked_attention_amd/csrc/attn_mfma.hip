@@ -6,7 +6,7 @@
 // end.  Each pair walks its share of the compacted list of kept key blocks
 // (CSR-like, ascending) in stages of KT keys:
 //   - K and V stage tiles go from HBM/L2 straight into LDS with
-//     global_load_lds_dwordx4 (no register staging): V two stages deep, K
+//     buffer_load_dwordx4 ... lds (no register staging): V two stages deep, K
 //     one, and the next K tile loads as soon as every wavefront has read
 //     this stage's K fragments (two barriers per stage, neither of which
 //     waits for tiles still in flight);
@@ -98,16 +98,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS-DMA of one 16-byte chunk per lane through a buffer resource based at
-// `base` (raw buffer, 32-bit data format; the range only has to cover the
-// stage tile): lane l's chunk at base + off lands at dst + 16 l.  The loads
-// of a tile share the scalar resource, so each is base plus the lane's
-// 32-bit offset with no per-load address arithmetic.
-__device__ __forceinline__ void chunk_to_lds(const uint16_t* base, uint32_t off, uint16_t* dst) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
 }
 
 // Workgroup barrier for the LDS stages.  __syncthreads() also waits for

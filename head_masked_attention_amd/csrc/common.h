@@ -156,6 +156,16 @@ __host__ __forceinline__ int64_t attn_grid(int64_t n_work, bool head_masked) {
     return ((n_work + kNumXcd - 1) / kNumXcd + (head_masked ? 1 : 0)) * kNumXcd;
 }
 
+// LDS-DMA of one 16-byte chunk per lane through a buffer resource based at
+// `base` (raw buffer, 32-bit data format; the range only has to cover the
+// stage tile): lane l's chunk at base + off lands at dst + 16 l.  The loads
+// of a tile share the scalar resource, so each is base plus the lane's
+// 32-bit offset with no per-load address arithmetic.
+__device__ __forceinline__ void chunk_to_lds(const void* base, uint32_t off, void* dst) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

@@ -541,7 +541,10 @@ void attn_mfma_kernel(AttnArgs a) {
 #define BSATTN_D128_KT 32
 #endif
 #ifndef BSATTN_D128_SPLIT
-#define BSATTN_D128_SPLIT 1
+#define BSATTN_D128_SPLIT 2
+#endif
+#ifndef BSATTN_D128_KM_WPE
+#define BSATTN_D128_KM_WPE 2
 #endif
 #ifndef BSATTN_D128_WPE
 #define BSATTN_D128_WPE 3
@@ -551,8 +554,8 @@ template <bool KMASK>
 static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128)
-        // the masked variant needs more registers: two waves per SIMD
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? 2 : BSATTN_D128_WPE,
+        // the masked variant needs a few more registers
+        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? BSATTN_D128_KM_WPE : BSATTN_D128_WPE,
                                        BSATTN_D128_BUF, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
     // the masked variant needs a few more registers

@@ -57,8 +57,9 @@ def profiled_traffic(workload: str):
     vals = {}
     with open(path) as f:
         for line in f:
-            if ":" in line and line.strip().startswith(("kernel_source_sha256", "traffic_bytes_per_launch")):
-                k, v = line.strip().split(":", 1)
+            line = line.strip().lstrip("- ")
+            if ":" in line and line.startswith(("kernel_source_sha256", "traffic_bytes_per_launch")):
+                k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip().strip("`")
     if vals.get("kernel_source_sha256") != attn_source_hash():
         return None

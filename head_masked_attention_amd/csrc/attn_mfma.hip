@@ -555,11 +555,11 @@ static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
     if (D == 128)
         // the masked variant needs a few more registers
-        return launch(attn_mfma_kernel<128, BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? BSATTN_D128_KM_WPE : BSATTN_D128_WPE,
+        return launch(attn_mfma_kernel<128, KMASK ? 32 : BSATTN_D128_KT, BSATTN_D128_SPLIT, KMASK ? BSATTN_D128_KM_WPE : BSATTN_D128_WPE,
                                        BSATTN_D128_BUF, KMASK>,
                       grid, dim3(128 * BSATTN_D128_SPLIT), s, a);
     // the masked variant needs a few more registers
-    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? BSATTN_D64_KM_WPE : BSATTN_D64_WPE,
+    return launch(attn_mfma_kernel<64, KMASK ? 32 : BSATTN_D64_KT, BSATTN_D64_SPLIT, KMASK ? BSATTN_D64_KM_WPE : BSATTN_D64_WPE,
                                    BSATTN_D64_BUF, KMASK>,
                   grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }

@@ -34,6 +34,9 @@ bsattn_status check_tensor(const bsattn_tensor* t, bool fp8 = false) {
     if (((uintptr_t)t->data) % 16 != 0) return BSATTN_ERR_STRIDE;
     if ((t->stride_b * es) % 16 || (t->stride_h * es) % 16 || (t->stride_n * es) % 16)
         return BSATTN_ERR_STRIDE;
+    // stage tiles are addressed as a base plus 32-bit lane offsets spanning up
+    // to 64 rows: row pitch below 32 MiB
+    if (t->stride_n * (int64_t)es >= (int64_t(1) << 25)) return BSATTN_ERR_STRIDE;
     return BSATTN_OK;
 }
 

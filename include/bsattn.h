@@ -63,7 +63,8 @@ typedef enum { BSATTN_BF16 = 0, BSATTN_F32 = 1, BSATTN_FP8_E4M3 = 2 } bsattn_dty
 /*
  * A device tensor viewed as [B][H][N][D].  Strides are in elements; the D
  * axis must be contiguous (stride 1).  `data` must be 16-byte aligned and
- * stride_n * element size must be a multiple of 16 bytes.
+ * stride_n * element size must be a multiple of 16 bytes and below 32 MiB
+ * (BSATTN_ERR_STRIDE otherwise).
  */
 typedef struct {
     void* data;

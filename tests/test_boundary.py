@@ -184,6 +184,7 @@ def test_forward_validation(lib):
         (dict(m=B_._BlockMask(1, 2, 4, 4, FAKE, 0, FAKE, 0, 0)), 1),
         (dict(scale=float("inf")), 6),
         (dict(q=tensor(sn=72, sh=256 * 72 + 4)), 4),
+        (dict(k=tensor(sn=1 << 24, sh=256 << 24)), 4),     # row pitch 32 MiB
     ]
     for over, code in cases:
         args = dict(q=tensor(), k=tensor(), v=tensor(), m=bmask(), out=tensor(), scale=0.0)

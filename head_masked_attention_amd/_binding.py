@@ -59,7 +59,7 @@ class _BlockMask(ctypes.Structure):
 
 EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
-           "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8",
+           "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8", "bsattn_forward_fp8_masked",
            "bsattn_head_mask", "bsattn_mask_density",
            "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
            "bsattn_stage_outcome_string"]
@@ -119,6 +119,9 @@ def load_library(path: str = LIB_PATH):
     lib.bsattn_forward_fp8.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                        P, P, P, ctypes.POINTER(_BlockMask), P, ctypes.c_float,
                                        ctypes.POINTER(_Tensor), P]
+    lib.bsattn_forward_fp8_masked.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                              ctypes.POINTER(_Tensor), P, P, P, ctypes.POINTER(_BlockMask), P,
+                                              P, i64, ctypes.c_float, ctypes.POINTER(_Tensor), P]
     lib.bsattn_head_mask.argtypes = [P, i32, dbl, i32, P]
     lib.bsattn_mask_density.argtypes = [ctypes.POINTER(_BlockMask), P, ctypes.POINTER(dbl)]
     lib.bsattn_stage_create.argtypes = [ctypes.POINTER(_StageConfig), ctypes.POINTER(P)]
@@ -280,16 +283,10 @@ def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale:
                                 ctypes.byref(to), _stream(q.device, stream))
         _check(st, "bsattn_forward")
         return out
-    if key_mask.dtype != torch.uint8 or not key_mask.is_cuda:
-        raise BsattnError(2, "bsattn_forward_masked", "key_mask must be a uint8 device tensor")
-    if key_mask.shape[-1] != q.shape[2] or key_mask.stride(-1) != 1 or key_mask.dim() not in (1, 2):
-        raise BsattnError(3, "bsattn_forward_masked", "key_mask must be [B, N] or [N] with unit key stride")
-    if key_mask.dim() == 2 and key_mask.shape[0] != q.shape[0]:
-        raise BsattnError(3, "bsattn_forward_masked", "key_mask batch must match q")
-    km_sb = 0 if key_mask.dim() == 1 or key_mask.shape[0] == 1 else key_mask.stride(0)
+    km, km_sb = _key_mask_arg(key_mask, q, "bsattn_forward_masked")
     st = lib.bsattn_forward_masked(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
-                                   None if bm is None else ctypes.byref(bm), hm, key_mask.data_ptr(),
-                                   int(km_sb), float(scale), ctypes.byref(to), _stream(q.device, stream))
+                                   None if bm is None else ctypes.byref(bm), hm, km, km_sb, float(scale),
+                                   ctypes.byref(to), _stream(q.device, stream))
     _check(st, "bsattn_forward_masked")
     return out
 
@@ -312,28 +309,53 @@ def quantize_fp8(x, *, out=None, scale=None, workspace=None, stream=None):
     return out, scale
 
 
+def _key_mask_arg(key_mask, q, where):
+    """(pointer, batch stride) of an optional uint8 device key mask [B, N] or [N]."""
+    import torch
+    if key_mask.dtype != torch.uint8 or not key_mask.is_cuda:
+        raise BsattnError(2, where, "key_mask must be a uint8 device tensor")
+    if key_mask.shape[-1] != q.shape[2] or key_mask.stride(-1) != 1 or key_mask.dim() not in (1, 2):
+        raise BsattnError(3, where, "key_mask must be [B, N] or [N] with unit key stride")
+    if key_mask.dim() == 2 and key_mask.shape[0] != q.shape[0]:
+        raise BsattnError(3, where, "key_mask batch must match q")
+    km_sb = 0 if key_mask.dim() == 1 or key_mask.shape[0] == 1 else key_mask.stride(0)
+    return key_mask.data_ptr(), int(km_sb)
+
+
 def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_mask: BlockMask | None = None, head_mask=None,
-                scale: float = 0.0, *, out=None, stream=None):
-    """bsattn_forward_fp8: attention on E4M3 inputs with per-(b, head) scales; bf16 output."""
+                scale: float = 0.0, *, out=None, stream=None, key_mask=None):
+    """bsattn_forward_fp8: attention on E4M3 inputs with per-(b, head) scales; bf16 output.
+
+    key_mask: optional uint8 device tensor [B, N] (or [N]); keys where it is 0
+    are masked in every row (bsattn_forward_fp8_masked).
+    """
     import torch
     lib = load_library()
+    where = "bsattn_forward_fp8" if key_mask is None else "bsattn_forward_fp8_masked"
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     for name, sc, heads in (("q_scale", q_scale, q8.shape[1]), ("k_scale", k_scale, k8.shape[1]),
                             ("v_scale", v_scale, v8.shape[1])):
         if sc.dtype != torch.float32 or not sc.is_cuda or not sc.is_contiguous() or sc.numel() != q8.shape[0] * heads:
-            raise BsattnError(3, "bsattn_forward_fp8", f"{name} must be a contiguous float32 device [B, heads]")
+            raise BsattnError(3, where, f"{name} must be a contiguous float32 device [B, heads]")
     hm = None
     if head_mask is not None:
         if head_mask.dtype != torch.uint8 or not head_mask.is_cuda or head_mask.numel() != q8.shape[1]:
-            raise BsattnError(3, "bsattn_forward_fp8", "head_mask must hold one byte per query head")
+            raise BsattnError(3, where, "head_mask must hold one byte per query head")
         hm = head_mask.data_ptr()
     tq, tk, tv, to = _tensor(q8), _tensor(k8), _tensor(v8), _tensor(out)
     bm = None if block_mask is None else block_mask._c()
-    st = lib.bsattn_forward_fp8(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q_scale.data_ptr(),
-                                k_scale.data_ptr(), v_scale.data_ptr(), None if bm is None else ctypes.byref(bm),
-                                hm, float(scale), ctypes.byref(to), _stream(q8.device, stream))
-    _check(st, "bsattn_forward_fp8")
+    if key_mask is None:
+        st = lib.bsattn_forward_fp8(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q_scale.data_ptr(),
+                                    k_scale.data_ptr(), v_scale.data_ptr(), None if bm is None else ctypes.byref(bm),
+                                    hm, float(scale), ctypes.byref(to), _stream(q8.device, stream))
+    else:
+        km, km_sb = _key_mask_arg(key_mask, q8, where)
+        st = lib.bsattn_forward_fp8_masked(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q_scale.data_ptr(),
+                                           k_scale.data_ptr(), v_scale.data_ptr(),
+                                           None if bm is None else ctypes.byref(bm), hm, km, km_sb, float(scale),
+                                           ctypes.byref(to), _stream(q8.device, stream))
+    _check(st, where)
     return out
 
 

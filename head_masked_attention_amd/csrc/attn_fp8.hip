@@ -20,6 +20,8 @@
 //     of a 16-lane group supplies 8 bytes of row 2e + J/2 ... so lane i
 //     receives byte column i of 8 consecutive rows).
 // Rows without kept blocks and heads with head_mask 0 are written as 0.
+// With a key mask (KMASK), a block whose 64 keys are all masked is skipped and
+// the masked keys of a partly masked block get -inf scores.
 //
 // Sources: SD.Next commit view, modules/attention/sparse, the stage paragraph
 // (a quantized kernel joins as a block-mask consumer) and the flex-consumer
@@ -65,7 +67,7 @@ __device__ __forceinline__ uint32_t f8_pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v_){lo, hi}, bf2v_));
 }
 
-template <int D, int WPE>
+template <int D, int WPE, bool KMASK>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float* __restrict__ k_scale,
                      const float* __restrict__ v_scale) {
@@ -155,8 +157,14 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
         koff[i] = (uint32_t)(r * (int32_t)a.k.sn + c * 16);
         voff[i] = (uint32_t)(r * (int32_t)a.v.sn + c * 16);
     }
+    // KMASK: each lane fetches the mask byte of one key of the stage's block
+    // with its tiles; at the stage a ballot makes it one wave-uniform 64-bit
+    // word (bit j = key j of the block live).
+    const uint8_t* kmbase = KMASK ? a.key_mask + (int64_t)b * a.km_sb : nullptr;
+    uint32_t km_next = 1u;
     auto issue = [&](int t, uint8_t* Kd, uint8_t* Vd) {
         const int64_t row0 = (int64_t)block_of(t) * BLK;
+        if constexpr (KMASK) km_next = (uint32_t)kmbase[row0 + lane];
         const uint8_t* kt = kbase + row0 * a.k.sn;
         const uint8_t* vt = vbase + row0 * a.v.sn;
 #pragma unroll
@@ -185,7 +193,10 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
     auto stage = [&](int t, const uint8_t* Kt, const uint8_t* Vt, uint8_t* Kn, uint8_t* Vn) {
         wait_vmcnt_f8();
         __syncthreads();
+        uint64_t kw = ~0ull;
+        if constexpr (KMASK) kw = __ballot(km_next != 0u);
         if (t + 1 < cnt) issue(t + 1, Kn, Vn);
+        if (KMASK && kw == 0ull) return;   // every key of the block masked
 
         // S^T: two 32-key tiles
         f16v8 sacc[2];
@@ -203,6 +214,19 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
                 const uint4 hi = *(const uint4*)(krow + (((c0 + 1) ^ sw) << 4));
                 const v8i kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], sacc[kt], 0, 0, 0, 127, 0, 127);
+            }
+        }
+
+        if constexpr (KMASK) {
+            // masked keys of a partly masked block: -inf scores (element r of
+            // tile kt is key 32 hl + 16 kt + r)
+            if (kw != ~0ull) {
+                const uint32_t wl = (uint32_t)(kw >> (32 * hl));
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (!((wl >> (16 * kt + r)) & 1u)) sacc[kt][r] = -INFINITY;
             }
         }
 
@@ -381,8 +405,12 @@ hipError_t launch_quant_fp8(TView x, TView y, int B, int H, int64_t N, int D, ui
 hipError_t launch_attn_fp8(const AttnArgs& a, int D, const float* qs, const float* ks, const float* vs,
                            hipStream_t s) {
     const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
-    if (D == 128) return launch(attn_fp8_kernel<128, 2>, grid, dim3(128), s, a, qs, ks, vs);
-    return launch(attn_fp8_kernel<64, 3>, grid, dim3(128), s, a, qs, ks, vs);
+    if (a.key_mask != nullptr) {
+        if (D == 128) return launch(attn_fp8_kernel<128, 2, true>, grid, dim3(128), s, a, qs, ks, vs);
+        return launch(attn_fp8_kernel<64, 3, true>, grid, dim3(128), s, a, qs, ks, vs);
+    }
+    if (D == 128) return launch(attn_fp8_kernel<128, 2, false>, grid, dim3(128), s, a, qs, ks, vs);
+    return launch(attn_fp8_kernel<64, 3, false>, grid, dim3(128), s, a, qs, ks, vs);
 }
 
 }  // namespace bsattn

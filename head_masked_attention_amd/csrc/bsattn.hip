@@ -256,6 +256,15 @@ bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k,
                                  const float* q_scale, const float* k_scale, const float* v_scale,
                                  const bsattn_block_mask* mask, const uint8_t* head_mask, float scale,
                                  bsattn_tensor* out, void* stream) {
+    return bsattn_forward_fp8_masked(q, k, v, q_scale, k_scale, v_scale, mask, head_mask, nullptr, 0, scale, out,
+                                     stream);
+}
+
+bsattn_status bsattn_forward_fp8_masked(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_tensor* v,
+                                        const float* q_scale, const float* k_scale, const float* v_scale,
+                                        const bsattn_block_mask* mask, const uint8_t* head_mask,
+                                        const uint8_t* key_mask, int64_t key_mask_stride_b, float scale,
+                                        bsattn_tensor* out, void* stream) {
     bsattn_status st;
     if ((st = check_tensor(q, true)) != BSATTN_OK) return st;
     if ((st = check_tensor(k, true)) != BSATTN_OK) return st;
@@ -277,6 +286,8 @@ bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k,
     }
     if (!std::isfinite(scale)) return BSATTN_ERR_BUDGET;
     if (k->stride_n > (1 << 24) || v->stride_n > (1 << 24)) return BSATTN_ERR_UNSUPPORTED;
+    if (key_mask != nullptr && (key_mask_stride_b < 0 || (key_mask_stride_b > 0 && key_mask_stride_b < q->N)))
+        return BSATTN_ERR_STRIDE;
     AttnArgs a;
     a.q = view_of(q);
     a.k = view_of(k);
@@ -295,8 +306,8 @@ bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k,
     a.count = mask ? mask->count : nullptr;
     a.index = mask ? mask->index : nullptr;
     a.head_mask = head_mask;
-    a.key_mask = nullptr;
-    a.km_sb = 0;
+    a.key_mask = key_mask;
+    a.km_sb = key_mask_stride_b;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     a.n_work = (int64_t)a.B * a.H * a.nqb;
     const hipError_t e = launch_attn_fp8(a, (int)q->D, q_scale, k_scale, v_scale, (hipStream_t)stream);

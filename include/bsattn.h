@@ -57,7 +57,7 @@ typedef enum {
 
 /* Element types of q, k, v and out.  FP8_E4M3 (OCP e4m3: 1 sign, 4 exponent
  * bits with bias 7, 3 mantissa bits, max 448, no infinities) is accepted only
- * by bsattn_quantize_fp8 (output) and bsattn_forward_fp8 (inputs). */
+ * by bsattn_quantize_fp8 (output) and bsattn_forward_fp8[_masked] (inputs). */
 typedef enum { BSATTN_BF16 = 0, BSATTN_F32 = 1, BSATTN_FP8_E4M3 = 2 } bsattn_dtype;
 
 /*
@@ -271,6 +271,22 @@ bsattn_status bsattn_forward_fp8(const bsattn_tensor* q, const bsattn_tensor* k,
                                  const float* q_scale, const float* k_scale, const float* v_scale,
                                  const bsattn_block_mask* mask, const uint8_t* head_mask, float scale,
                                  bsattn_tensor* out, void* stream);
+
+/*
+ * bsattn_forward_fp8 with a per-token key mask composed with the block mask
+ * (SD.Next sparse-stage paragraph: the token attention mask and the block
+ * mask go to the consumer together; here the quantized one).  key_mask and
+ * key_mask_stride_b as in bsattn_forward_masked: device uint8,
+ * key_mask[b * key_mask_stride_b + j], 0 masks key j; stride >= N or 0 for a
+ * mask shared by the batch; NULL behaves exactly as bsattn_forward_fp8.  A
+ * row whose kept keys are all masked is written as 0.  Errors as
+ * bsattn_forward_fp8, plus BSATTN_ERR_STRIDE when 0 < key_mask_stride_b < N.
+ */
+bsattn_status bsattn_forward_fp8_masked(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_tensor* v,
+                                        const float* q_scale, const float* k_scale, const float* v_scale,
+                                        const bsattn_block_mask* mask, const uint8_t* head_mask,
+                                        const uint8_t* key_mask, int64_t key_mask_stride_b, float scale,
+                                        bsattn_tensor* out, void* stream);
 
 /*
  * Per-layer head mask (haagenti_sparse AttentionMask / MaskBuilder with

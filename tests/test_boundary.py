@@ -216,6 +216,12 @@ def test_fp8_entry_points_validation(lib):
     assert fwd8(f8(), f8(), f8(), tensor(dtype=B_.F32)) == 2     # out must be bf16
     assert fwd8(f8(), f8(), f8(), tensor(), scales=(None, FAKE, FAKE)) == 1
     assert fwd8(f8(D=32), f8(D=32), f8(D=32), tensor(D=32)) == 9  # no kernel for D = 32
+    fwd8m = lambda km, sb, q=None: lib.bsattn_forward_fp8_masked(
+        ctypes.byref(q or f8()), ctypes.byref(f8()), ctypes.byref(f8()), FAKE, FAKE, FAKE, ctypes.byref(m),
+        None, km, sb, 0.0, ctypes.byref(tensor()), None)
+    assert fwd8m(FAKE, 100) == 4                  # key-mask batch stride shorter than N = 256
+    assert fwd8m(FAKE, -256) == 4
+    assert fwd8m(FAKE, 256, q=tensor()) == 2      # tensor checks come first
     # the bf16/fp32 entry points refuse E4M3 codes
     assert call_forward(lib, f8(), f8(), f8(), m, tensor()) == 2
     x, y = tensor(), f8()

@@ -103,3 +103,61 @@ def test_forward_fp8_dense_sdxl_shape(cuda):
     ref = oracle.attention(*deq, 64, bm.mask.cpu().numpy(), rows=rows)
     got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
     check(got, ref, "sdxl sampled rows")
+
+
+def key_mask_fp8(B, N, seed):
+    """Live keys with the structure of padded prompts: a masked tail per batch,
+    one wholly masked 64-key block, one partly masked block, random holes."""
+    rng = np.random.default_rng(seed)
+    km = (rng.random((B, N)) < 0.85).astype(np.uint8)
+    km[:, 64:128] = 0                              # a whole key block masked
+    km[:, 128:160] = 0                             # half of the next one
+    km[-1, N - 96:] = 0                            # a masked tail on the last batch entry
+    return km
+
+
+@pytest.mark.parametrize("case", CASES[:2] + CASES[2:3], ids=[c[0] for c in CASES[:2] + CASES[2:3]])
+def test_forward_fp8_key_mask(cuda, case):
+    name, B, H, Hkv, N, D, density = case
+    q, k, v = workloads.small_case(B=B, H=H, Hkv=Hkv, N=N, D=D, seed=76)
+    nb = N // 64
+    rng = np.random.default_rng(77)
+    mask = (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
+    mask[:, :, :, 1] = 1                           # every row keeps the wholly masked block
+    mask[0, 0, 3, :] = 0
+    mask[0, 0, 3, 1] = 1                           # a row whose only kept block is wholly masked
+    hmask = workloads.random_head_mask(H, seed=78)
+    km = key_mask_fp8(B, N, 79)
+    q8, qs = hm.quantize_fp8(q.to(cuda))
+    k8, ks = hm.quantize_fp8(k.to(cuda))
+    v8, vs = hm.quantize_fp8(v.to(cuda))
+    out = hm.forward_fp8(q8, k8, v8, qs, ks, vs, upload_mask(mask, cuda), torch.from_numpy(hmask).to(cuda),
+                         key_mask=torch.from_numpy(km).to(cuda))
+    torch.cuda.synchronize()
+    deq = [oracle.dequantize_e4m3(c.cpu().numpy(), s.cpu().numpy()) for c, s in ((q8, qs), (k8, ks), (v8, vs))]
+    ref = oracle.attention(*deq, 64, mask, head_mask=hmask, key_mask=km)
+    got = to64(out)
+    check(got, ref, name + " key mask")
+    assert np.all(got[:, hmask == 0] == 0)
+    if hmask[0]:
+        assert np.all(got[0, 0, 3 * 64:4 * 64] == 0)   # every kept key masked: zero row
+
+
+def test_forward_fp8_key_mask_all_live_and_shared(cuda):
+    B, H, N, D = 2, 2, 64 * 8, 128
+    q, k, v = workloads.small_case(B=B, H=H, N=N, D=D, seed=80)
+    nb = N // 64
+    mask = (np.random.default_rng(81).random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+    bm = upload_mask(mask, cuda)
+    q8, qs = hm.quantize_fp8(q.to(cuda))
+    k8, ks = hm.quantize_fp8(k.to(cuda))
+    v8, vs = hm.quantize_fp8(v.to(cuda))
+    plain = hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm)
+    live = hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm, key_mask=torch.ones(B, N, dtype=torch.uint8, device=cuda))
+    km1 = key_mask_fp8(1, N, 82)[0]
+    shared = hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm, key_mask=torch.from_numpy(km1).to(cuda))
+    torch.cuda.synchronize()
+    assert torch.equal(plain, live)               # all-live stages run the unmasked arithmetic
+    deq = [oracle.dequantize_e4m3(c.cpu().numpy(), s.cpu().numpy()) for c, s in ((q8, qs), (k8, ks), (v8, vs))]
+    ref = oracle.attention(*deq, 64, mask, key_mask=km1)
+    check(to64(shared), ref, "shared key mask")

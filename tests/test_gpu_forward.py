@@ -159,7 +159,7 @@ def test_forward_large_workload_sampled(cuda, name):
         assert torch.all(got[:, :, qb * w.block:(qb + 1) * w.block] == 0)
 
 
-@pytest.mark.parametrize("name", ["video_radial_bf16"])
+@pytest.mark.parametrize("name", ["video_radial_bf16", "video_gqa_bf16"])
 def test_forward_radial_mask_sampled(cuda, name):
     w = workloads.ALL[name]
     q, k, v = workloads.make_qkv(w)

@@ -82,7 +82,7 @@ STACK = Workload(
 VIDEO_GQA = Workload(
     name="video_gqa_bf16", B=1, H=24, N=33280, D=128, block=64, dtype="bf16", budget=0.3,
     segments=(("text", 128), ("padding", 384), ("video", 32768)),
-    grid=(8, 64, 64), Hkv=6,
+    grid=(8, 64, 64), Hkv=6, radial=True,
     notes="the video length with grouped K/V heads (4 query heads per K/V head)")
 
 ALL = {w.name: w for w in (TINY, SDXL, JOINT, VIDEO, STACK, VIDEO_GQA)}

@@ -30,6 +30,11 @@
 #include "common.h"
 #include "internal.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
+
 namespace bsattn {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -70,7 +75,7 @@ __device__ __forceinline__ uint32_t f8_pack_bf16x2(float lo, float hi) {
 template <int D, int WPE, bool KMASK>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float* __restrict__ k_scale,
-                     const float* __restrict__ v_scale) {
+                     const float* __restrict__ v_scale, int one_round) {
     constexpr int BLK = 64;                  // keys per stage = one key block
     constexpr int CPR = D / 16;              // 16-byte chunks per fp8 row
     constexpr int NI = BLK * CPR / 128;      // DMA loads per thread per tensor per stage
@@ -191,6 +196,16 @@ void attn_fp8_kernel(AttnArgs a, const float* __restrict__ q_scale, const float*
     const int g16 = lane >> 4, j16 = lane & 15;
 
     auto stage = [&](int t, const uint8_t* Kt, const uint8_t* Vt, uint8_t* Kn, uint8_t* Vn) {
+        if (one_round) {
+            // issue priority 3..0 over the quarters of the row's blocks, so
+            // that the workgroups of a CU, which start together, stay abreast
+            // (with several rounds it only delays the ones about to finish)
+            const int pr = 3 - min(3, (4 * t) / cnt);
+            if (pr == 3) __builtin_amdgcn_s_setprio(3);
+            else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+            else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         wait_vmcnt_f8();
         __syncthreads();
         uint64_t kw = ~0ull;
@@ -402,15 +417,38 @@ hipError_t launch_quant_fp8(TView x, TView y, int B, int H, int64_t N, int D, ui
     return e;
 }
 
+// Workgroups of `kernel` resident on the device at once (CUs x occupancy),
+// queried once per device and kernel.
+template <typename K>
+static int64_t resident_workgroups(K kernel, int threads) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const std::pair<int, const void*> key{dev, (const void*)kernel};
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        return 0;
+    return cache[key] = (int64_t)cus * per_cu;
+}
+
+template <int D, int WPE, bool KMASK>
+static hipError_t launch_attn_fp8_t(const AttnArgs& a, const float* qs, const float* ks, const float* vs,
+                                    hipStream_t s) {
+    const int64_t n = attn_grid(a.n_work, a.head_mask != nullptr);
+    const int one_round = n <= resident_workgroups(attn_fp8_kernel<D, WPE, KMASK>, 128) ? 1 : 0;
+    return launch(attn_fp8_kernel<D, WPE, KMASK>, dim3((unsigned)n), dim3(128), s, a, qs, ks, vs, one_round);
+}
+
 hipError_t launch_attn_fp8(const AttnArgs& a, int D, const float* qs, const float* ks, const float* vs,
                            hipStream_t s) {
-    const dim3 grid((unsigned)attn_grid(a.n_work, a.head_mask != nullptr));
-    if (a.key_mask != nullptr) {
-        if (D == 128) return launch(attn_fp8_kernel<128, 2, true>, grid, dim3(128), s, a, qs, ks, vs);
-        return launch(attn_fp8_kernel<64, 3, true>, grid, dim3(128), s, a, qs, ks, vs);
-    }
-    if (D == 128) return launch(attn_fp8_kernel<128, 2, false>, grid, dim3(128), s, a, qs, ks, vs);
-    return launch(attn_fp8_kernel<64, 3, false>, grid, dim3(128), s, a, qs, ks, vs);
+    if (a.key_mask != nullptr)
+        return D == 128 ? launch_attn_fp8_t<128, 2, true>(a, qs, ks, vs, s) : launch_attn_fp8_t<64, 3, true>(a, qs, ks, vs, s);
+    return D == 128 ? launch_attn_fp8_t<128, 2, false>(a, qs, ks, vs, s) : launch_attn_fp8_t<64, 3, false>(a, qs, ks, vs, s);
 }
 
 }  // namespace bsattn

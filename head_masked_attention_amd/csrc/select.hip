@@ -116,6 +116,28 @@ __device__ __forceinline__ uint32_t orderable(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The value of lane (lane ^ m), m a power of two below 64 known at compile
+// time after unrolling, without the LDS crossbar where the VALU can do it:
+// DPP quad permutes for 1 and 2, mirror compositions for 4 (i ^ 7 ^ 3) and 8
+// (i ^ 15 ^ 7), a swizzle for 16 and the half swap for 32 (which returns the
+// lower half's value first and the upper half's second, on every lane).
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
+    switch (m) {
+    case 1: return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
+    case 2: return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
+    case 4: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
+                                            0x1B, 0xF, 0xF, false);            // row_half_mirror, quad_perm [3,2,1,0]
+    case 8: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false),
+                                            0x141, 0xF, 0xF, false);           // row_mirror, row_half_mirror
+    case 16: return __builtin_amdgcn_ds_swizzle(x, 0x1F | (0x10 << 10));        // bit mode, xor 16
+    case 32: {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    }
+    default: return __shfl_xor(x, m);
+    }
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     uint32_t lo = __shfl_xor((uint32_t)v, m);
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
@@ -248,7 +270,7 @@ __device__ __forceinline__ void wave_bitonic_desc32(uint32_t (&key)[R][E], int l
 #pragma unroll
                     for (int r = 0; r < E; ++r) {
                         const int e = lane * E + r;
-                        const uint32_t other = __shfl_xor(key[q][r], lm);
+                        const uint32_t other = lane_xor(key[q][r], lm);
                         const bool take_max = ((e & stride) == 0) == ((e & size) == 0);
                         key[q][r] = take_max ? max(key[q][r], other) : min(key[q][r], other);
                     }

@@ -39,6 +39,28 @@ __device__ __forceinline__ int64_t pooled_offset(int32_t p, int32_t d) {
     return (int64_t)(p >> 4) * 16 * D + ((c * 4 + gq) * 16 + li) * 4 + e;
 }
 
+// The value of lane (lane ^ m), m a power of two below 64 known at compile
+// time after unrolling, without the LDS crossbar where the VALU can do it:
+// DPP quad permutes for 1 and 2, mirror compositions for 4 (i ^ 7 ^ 3) and 8
+// (i ^ 15 ^ 7), a swizzle for 16 and the half swap for 32 (which returns the
+// lower half's value first and the upper half's second, on every lane).
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
+    switch (m) {
+    case 1: return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
+    case 2: return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
+    case 4: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
+                                            0x1B, 0xF, 0xF, false);            // row_half_mirror, quad_perm [3,2,1,0]
+    case 8: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false),
+                                            0x141, 0xF, 0xF, false);           // row_mirror, row_half_mirror
+    case 16: return __builtin_amdgcn_ds_swizzle(x, 0x1F | (0x10 << 10));        // bit mode, xor 16
+    case 32: {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    }
+    default: return __shfl_xor(x, m);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K1: block sums.  One wavefront per (tensor, b, head, candidate block).
 // Ranking by <sum Q_i, sum K_j> equals ranking by the mean-pooled score: the
@@ -99,7 +121,7 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+        for (int e = 0; e < EPC; ++e) acc[e] += __uint_as_float(lane_xor(__float_as_uint(acc[e]), off));
 
     if (lane < CPR) {
 #pragma unroll
@@ -114,28 +136,6 @@ __device__ __forceinline__ uint32_t orderable(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u << 1) == 0) u = 0;                       // -0 -> +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The value of lane (lane ^ m), m a power of two below 64 known at compile
-// time after unrolling, without the LDS crossbar where the VALU can do it:
-// DPP quad permutes for 1 and 2, mirror compositions for 4 (i ^ 7 ^ 3) and 8
-// (i ^ 15 ^ 7), a swizzle for 16 and the half swap for 32 (which returns the
-// lower half's value first and the upper half's second, on every lane).
-__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
-    switch (m) {
-    case 1: return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
-    case 2: return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
-    case 4: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
-                                            0x1B, 0xF, 0xF, false);            // row_half_mirror, quad_perm [3,2,1,0]
-    case 8: return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false),
-                                            0x141, 0xF, 0xF, false);           // row_mirror, row_half_mirror
-    case 16: return __builtin_amdgcn_ds_swizzle(x, 0x1F | (0x10 << 10));        // bit mode, xor 16
-    case 32: {
-        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        return (__lane_id() & 32) ? r[0] : r[1];
-    }
-    default: return __shfl_xor(x, m);
-    }
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {

@@ -55,38 +55,86 @@ struct MaskOut {
 };
 
 // ---- run lookups (runs are few; a linear scan is cheapest) ----------------
+// The fields of the first kFastRuns runs are read at constant indices into
+// SGPRs: wave-uniform scalar loads that the compiler issues with the other
+// kernel arguments.  Indexed reads would be per-lane vector loads of the
+// uncached argument block, one dependent round trip each, whenever lanes look
+// up different blocks.  (The empty asm keeps the optimizer from folding the
+// reads of different runs back into one indexed load.)  Runs past kFastRuns,
+// layouts of many segments, take the indexed loop.
+constexpr int kFastRuns = 4;
+
+struct Run {
+    int32_t first, len, cls, off;
+};
+__device__ __forceinline__ int32_t pin_sgpr(int32_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+template <int R>
+__device__ __forceinline__ Run fast_run(const Geometry& g) {
+    return {pin_sgpr(g.run_first[R]), pin_sgpr(g.run_len[R]), pin_sgpr(g.run_cls[R]), pin_sgpr(g.run_off[R])};
+}
+__device__ __forceinline__ Run slow_run(const Geometry& g, int r) {
+    return {g.run_first[r], g.run_len[r], g.run_cls[r], g.run_off[r]};
+}
+
+// f(run) returns true when the run answers the lookup (it stores the answer);
+// runs are visited in order and the first answer wins.
+template <typename F>
+__device__ __forceinline__ bool visit_runs(const Geometry& g, F f) {
+    if (g.n_runs > 0 && f(fast_run<0>(g))) return true;
+    if (g.n_runs > 1 && f(fast_run<1>(g))) return true;
+    if (g.n_runs > 2 && f(fast_run<2>(g))) return true;
+    if (g.n_runs > 3 && f(fast_run<3>(g))) return true;
+    static_assert(kFastRuns == 4, "fast runs visited above");
+    for (int r = kFastRuns; r < g.n_runs; ++r)
+        if (f(slow_run(g, r))) return true;
+    return false;
+}
 
 __device__ __forceinline__ int32_t block_class(const Geometry& g, int32_t j) {
-    for (int r = 0; r < g.n_runs; ++r)
-        if (j < g.run_first[r] + g.run_len[r]) return g.run_cls[r];
-    return CLS_DROPPED;
+    int32_t cls = CLS_DROPPED;
+    visit_runs(g, [&](const Run& u) {
+        if (j >= u.first + u.len) return false;
+        cls = u.cls;
+        return true;
+    });
+    return cls;
 }
 
 // Block index of the pos-th SPARSE block.
 __device__ __forceinline__ int32_t cand_block(const Geometry& g, int32_t pos) {
-    for (int r = 0; r < g.n_runs; ++r)
-        if (g.run_cls[r] == CLS_SPARSE && pos < g.run_off[r] + g.run_len[r])
-            return g.run_first[r] + (pos - g.run_off[r]);
-    return -1;
+    int32_t blk = -1;
+    visit_runs(g, [&](const Run& u) {
+        if (u.cls != CLS_SPARSE || pos >= u.off + u.len) return false;
+        blk = u.first + (pos - u.off);
+        return true;
+    });
+    return blk;
 }
 
 // Block index of the pos-th non-SPARSE block.
 __device__ __forceinline__ int32_t other_block(const Geometry& g, int32_t pos) {
-    for (int r = 0; r < g.n_runs; ++r)
-        if (g.run_cls[r] != CLS_SPARSE && pos < g.run_off[r] + g.run_len[r])
-            return g.run_first[r] + (pos - g.run_off[r]);
-    return -1;
+    int32_t blk = -1;
+    visit_runs(g, [&](const Run& u) {
+        if (u.cls == CLS_SPARSE || pos >= u.off + u.len) return false;
+        blk = u.first + (pos - u.off);
+        return true;
+    });
+    return blk;
 }
 
 // Column code used by the compaction passes: candidate position (>= 0) for a
 // SPARSE block, -1 for PINNED, -2 for DROPPED.
 __device__ __forceinline__ int32_t column_code(const Geometry& g, int32_t j) {
-    for (int r = 0; r < g.n_runs; ++r)
-        if (j < g.run_first[r] + g.run_len[r]) {
-            if (g.run_cls[r] == CLS_SPARSE) return g.run_off[r] + (j - g.run_first[r]);
-            return g.run_cls[r] == CLS_PINNED ? -1 : -2;
-        }
-    return -2;
+    int32_t code = -2;
+    visit_runs(g, [&](const Run& u) {
+        if (j >= u.first + u.len) return false;
+        code = u.cls == CLS_SPARSE ? u.off + (j - u.first) : (u.cls == CLS_PINNED ? -1 : -2);
+        return true;
+    });
+    return code;
 }
 
 // XCD-aware workgroup order: hardware workgroup w runs on XCD w % 8, so the

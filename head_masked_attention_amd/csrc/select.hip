@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     static_assert(CPR <= 64 && 64 % CPR == 0 && BLOCK % RPI == 0, "pool geometry");
 
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // wave-uniform, so that the run lookup below is scalar
+    const int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t nq = (int64_t)B * H * g.n_cand;
     const int64_t nk = (int64_t)B * Hkv * g.n_cand;
     if (item >= nq + nk) return;
@@ -192,6 +193,10 @@ constexpr int kCodeTable = 1024;
 // 32-bit store per lane (vec4: nb % 4 == 0 and a 4-byte aligned mask), and a
 // lane's slot in the index list is the wavefront prefix sum of the per-lane
 // counts (0..4), taken bit-plane by bit-plane with ballots.
+// The pass is branch-free so that its LDS reads overlap: the four codes come
+// in one 8-byte read of the code table, and keep() is evaluated for every
+// column at a clamped code (>= 0; an LDS read in keep() stays in its row)
+// and its result used only for live SPARSE columns.
 template <typename KeepFn>
 __device__ __forceinline__ void compact_row(const Geometry& g, const int16_t* codes, bool vec4, int lane,
                                             bool row_dropped, bool row_pinned, uint8_t* mrow,
@@ -200,18 +205,32 @@ __device__ __forceinline__ void compact_row(const Geometry& g, const int16_t* co
     int32_t cnt = 0;
     for (int32_t j0 = 0; j0 < g.nb; j0 += 256) {
         const int32_t jl = j0 + 4 * lane;
+        int32_t code[4];
+        if (codes != nullptr) {
+            // jl + 3 < kCodeTable: j0 < nb <= kCodeTable and j0 % 256 == 0
+            const uint2 c4 = *(const uint2*)(codes + jl);
+            code[0] = (int32_t)(int16_t)(c4.x & 0xffffu);
+            code[1] = (int32_t)(int16_t)(c4.x >> 16);
+            code[2] = (int32_t)(int16_t)(c4.y & 0xffffu);
+            code[3] = (int32_t)(int16_t)(c4.y >> 16);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) code[u] = jl + u < g.nb ? column_code(g, jl + u) : -2;
+        }
+        // table entries past nb are never used
+#pragma unroll
+        for (int u = 0; u < 4; ++u) code[u] = jl + u < g.nb && !row_dropped ? code[u] : -2;
+        uint32_t kbits = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kbits |= (uint32_t)keep(jl + u, code[u] > 0 ? code[u] : 0) << u;
+        // the empty asm keeps the four keep() evaluations (LDS reads) ahead
+        // of the branches below, so that they are waited for once
+        asm volatile("" : "+v"(kbits));
         uint32_t bits = 0;
         int c = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int32_t j = jl + u;
-            bool v = false;
-            if (j < g.nb && !row_dropped) {
-                const int32_t code = codes != nullptr ? (int32_t)codes[j] : column_code(g, j);
-                if (code == -2) v = false;
-                else if (code == -1 || row_pinned) v = true;
-                else v = keep(j, code);
-            }
+            const bool v = code[u] != -2 && (code[u] == -1 || row_pinned || ((kbits >> u) & 1u));
             bits |= (uint32_t)v << (8 * u);
             c += v ? 1 : 0;
         }
@@ -280,13 +299,20 @@ __device__ __forceinline__ void wave_bitonic_desc32(uint32_t (&key)[R][E], int l
 }
 
 // Rows per workgroup and wavefronts per workgroup of the score/rank kernel:
-// one 16-row MFMA tile per workgroup, two rows per wavefront (more
-// workgroups beat longer ones: 32-row tiles took 32 -> 26 us on the joint
-// text+image shape and 100 -> 70 us on the video shape).
+// one 16-row MFMA tile per workgroup (more workgroups beat longer ones:
+// 32-row tiles took 32 -> 26 us on the joint text+image shape and 100 -> 70 us
+// on the video shape).  Up to 128 candidates each wavefront ranks and
+// compacts one row; the compaction of a row is a few hundred dependent scalar
+// and vector instructions, so rows compact side by side rather than one after
+// another.  Longer rows are ranked two at a time by one wavefront, whose
+// interleaved sorting networks hide each other's exchange latency.
+#ifndef BSATTN_RANK_ONE_ROW_EMAX
+#define BSATTN_RANK_ONE_ROW_EMAX 2
+#endif
 template <int E>
 struct RankShape {
     static constexpr int RT = 16;
-    static constexpr int WAVES = 8;
+    static constexpr int WAVES = E <= BSATTN_RANK_ONE_ROW_EMAX ? 16 : 8;
 };
 
 // ---------------------------------------------------------------------------
@@ -311,12 +337,14 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     constexpr int WAVES = RankShape<E>::WAVES;
     constexpr bool K32 = E <= 8;
     constexpr int RPW = RT / WAVES;            // rows per wavefront
+    constexpr int RR = RPW >= 2 ? 2 : 1;       // rows ranked together (32-bit keys)
     constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
     constexpr int KQ = D / 4;                  // MFMA k-steps; lane group gq owns d in [gq*KQ, gq*KQ+KQ)
-    static_assert(RPW >= 1 && (!K32 || RPW % 2 == 0), "rows per wavefront");
+    static_assert(RPW >= 1 && RPW % RR == 0, "rows per wavefront");
     __shared__ float s_score[RT * SSTR];
-    __shared__ uint8_t s_keep[WAVES][K32 ? 2 : 1][NPAD];
-    __shared__ int16_t s_code[kCodeTable];
+    __shared__ uint8_t s_keep[WAVES][K32 ? RR : 1][NPAD];
+    __shared__ __attribute__((aligned(8))) int16_t s_code[kCodeTable];
+    __shared__ int32_t s_rowblk[RT];             // block index of each row of the tile
     const int16_t* codes = fill_codes(g, s_code);
     const bool vec4 = (g.nb & 3) == 0 && ((uintptr_t)out.mask & 3u) == 0;
 
@@ -327,6 +355,9 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const int64_t g_kv = h / (H / Hkv);
     const int p0 = tile * RT;
     const int rows = min(RT, g.n_cand - p0);
+    // looked up here, next to the operand loads, rather than at each row's
+    // compaction, where every argument read would wait a memory round trip
+    if (threadIdx.x < RT) s_rowblk[threadIdx.x] = cand_block(g, p0 + (int)threadIdx.x);
 
     const int64_t prow = pooled_rows(g.n_cand);
     const float* qbase = qp + bh * prow * D;
@@ -375,7 +406,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const int64_t nb = g.nb;
     const int32_t w = g.w;
     auto compact_sparse = [&](int p, const uint8_t* keep_row) {
-        const int32_t i = cand_block(g, p);
+        const int32_t i = __builtin_amdgcn_readfirstlane(s_rowblk[p - p0]);
         compact_row(g, codes, vec4, lane, false, false, out.mask + (slice * nb + i) * nb,
                     out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
                     [&](int32_t j, int32_t code) {
@@ -384,13 +415,13 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     };
 
     if constexpr (K32) {
-        // ---- two rows at a time per wavefront
+        // ---- RR rows at a time per wavefront
         constexpr int IB = __builtin_ctz(NPAD);            // index bits
         constexpr uint32_t IMASK = (1u << IB) - 1u;
-        for (int r0 = wave * RPW; r0 < wave * RPW + RPW; r0 += 2) {
-            uint32_t key[2][E];
+        for (int r0 = wave * RPW; r0 < wave * RPW + RPW; r0 += RR) {
+            uint32_t key[RR][E];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < RR; ++q) {
                 const int rl = r0 + q;
                 const int p = p0 + rl;
 #pragma unroll
@@ -404,22 +435,22 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
                     key[q][r] = kv;
                 }
             }
-            wave_bitonic_desc32<2, E>(key, lane);
+            wave_bitonic_desc32<RR, E>(key, lane);
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < RR; ++q)
 #pragma unroll
                 for (int r = 0; r < E; ++r) s_keep[wave][q][lane * E + r] = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < RR; ++q)
 #pragma unroll
                 for (int r = 0; r < E; ++r)
                     if (lane * E + r < g.k && r0 + q < rows) s_keep[wave][q][IMASK - (key[q][r] & IMASK)] = 1;
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < RR; ++q)
                 if (r0 + q < rows) compact_sparse(p0 + r0 + q, s_keep[wave][q]);
             __builtin_amdgcn_wave_barrier();
         }
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
 // the window; k = n_cand gives the dense (layout-only) mask.  grid.y = slice.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
-    __shared__ int16_t s_code[kCodeTable];
+    __shared__ __attribute__((aligned(8))) int16_t s_code[kCodeTable];
     const int16_t* codes = fill_codes(g, s_code);
     __syncthreads();
     const bool vec4 = (g.nb & 3) == 0 && ((uintptr_t)out.mask & 3u) == 0;

@@ -12,9 +12,11 @@
 //     waits for tiles still in flight);
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the Q^T fragments held in
 //     VGPRs for the whole loop;
-//   - online softmax in fp32: exp2 with the scale folded into log2 units, and
-//     the running output rescaled only when a row maximum grows by more than
-//     2^8 (exponentials stay <= 256, exact after the final division);
+//   - online softmax in fp32: exp2 with the scale folded into log2 units,
+//     exponentials taken against the running row maximum, which is raised
+//     (and the running output rescaled) only on a row's first live stage or
+//     when a stage's exponentials sum past 2^16; exact after the final
+//     division, so the row maximum is not computed on most stages;
 //   - O^T += V^T P^T with the V^T fragments read by ds_read_b64_tr_b16 from
 //     the row-major V tile, so V is never transposed in memory.
 // Every lane holds one query's scores and one query's output column; the
@@ -148,7 +150,7 @@ void attn_mfma_kernel(AttnArgs a) {
     constexpr int NDT = D / 32;              // 32-row d tiles of O^T
     constexpr int NPS = KT / 16;             // 16-key steps of O^T per stage
     constexpr int SUB = BLK / KT;            // stages per key block
-    constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
+    constexpr float kSumCap = 65536.0f;      // largest stage sum of exponentials kept per lane
     static_assert(NI >= 1 && KT * CPR % LT == 0, "stage tiling");
     static_assert(!SHARE || SPLIT == 2, "two query heads per workgroup");
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
@@ -423,54 +425,76 @@ void attn_mfma_kernel(AttnArgs a) {
             }
         }
 
-        // online softmax with lazy rescaling; the row maximum as a tree of
-        // three-input maxima (v_max3_f32)
-        float mk[NKT];
+        // Online softmax.  P = exp2(S * scale * log2(e) - m_run) in bf16, packed
+        // as the B operand of P V (one per 16-key step); the stage's row sums
+        // come from bf16 dot products of the same packed values.
+        bf16x8 pf[NPS];
+        const bf2v one2 = {(__bf16)1.f, (__bf16)1.f};
+        auto make_p = [&]() -> float {
+            float psum2[2] = {0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            const f16v& x = sacc[kt];
-            const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-            const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
-            const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-            mk[kt] = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
-        }
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int kt = 1; kt < NKT; ++kt) mk[0] = fmaxf(mk[0], mk[kt]);
-        const float mx = pair_max32(mk[0]) * sl2;
-        const bool grow = mx > m_run + kTau;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
-            const float m_new = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                for (int u = 0; u < 2; ++u) {
+                    bf2v w[4];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_run));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_run));
+                        w[e >> 1] = to_bf16x2(p0, p1);
+                        psum2[(e >> 1) & 1] =
+                            __builtin_amdgcn_fdot2_f32_bf16(w[e >> 1], one2, psum2[(e >> 1) & 1], false);
+                    }
+                    pf[2 * kt + u] = __builtin_bit_cast(
+                        bf16x8, (uint4){__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
+                                        __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3])});
+                }
+            return psum2[0] + psum2[1];
+        };
+        // Exact step: the row maximum of the stage (a tree of three-input
+        // maxima, then the lane pair), the running maximum raised to it, and
+        // the running sum and output rescaled by exp2(old - new).
+        auto raise_max = [&]() {
+            float mk[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const f16v& x = sacc[kt];
+                const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+                const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+                const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+                mk[kt] = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
+            }
+#pragma unroll
+            for (int kt = 1; kt < NKT; ++kt) mk[0] = fmaxf(mk[0], mk[kt]);
+            const float m_new = fmaxf(m_run, pair_max32(mk[0]) * sl2);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        }
-
-        // P in bf16, packed as the B operand of P V (one per 16-key step);
-        // row sums from bf16 dot products of the same packed values
-        bf16x8 pf[NPS];
-        float psum2[2] = {0.f, 0.f};
-        const bf2v one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bf2v w[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e], sl2, -m_run));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * u + e + 1], sl2, -m_run));
-                    w[e >> 1] = to_bf16x2(p0, p1);
-                    psum2[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(w[e >> 1], one2, psum2[(e >> 1) & 1], false);
-                }
-                pf[2 * kt + u] = __builtin_bit_cast(
-                    bf16x8, (uint4){__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
-                                    __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3])});
+        };
+        // The running maximum is only raised when it must be.  A row's first
+        // live stage takes the exact step.  Later stages exponentiate against
+        // the current maximum and check the lane's stage sum: at most kSumCap
+        // (every exponential <= kSumCap, so the fp32 sums and outputs stay far
+        // from overflow; their relative precision does not depend on the
+        // scale) keeps the values, otherwise (a score far above the running
+        // maximum, an overflow to inf included) the stage takes the exact step
+        // and exponentiates again.  Each branch is wave-uniform.
+        float ps;
+        if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
+            raise_max();
+            ps = make_p();
+        } else {
+            ps = make_p();
+            if (__builtin_amdgcn_ballot_w64(ps > kSumCap) != 0) {
+                raise_max();
+                ps = make_p();
             }
-        l_run += psum2[0] + psum2[1];
+        }
+        l_run += ps;
 
         if constexpr (BUF == BUF_V1) {
             // this stage's V has landed; the next stage's K may still fly

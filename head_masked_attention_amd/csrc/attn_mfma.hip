@@ -151,6 +151,7 @@ void attn_mfma_kernel(AttnArgs a) {
     constexpr int NPS = KT / 16;             // 16-key steps of O^T per stage
     constexpr int SUB = BLK / KT;            // stages per key block
     constexpr float kSumCap = 65536.0f;      // largest stage sum of exponentials kept per lane
+    constexpr float kTau = 8.0f;             // key-mask variant: lazy-rescale threshold (log2 units)
     static_assert(NI >= 1 && KT * CPR % LT == 0, "stage tiling");
     static_assert(!SHARE || SPLIT == 2, "two query heads per workgroup");
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
@@ -454,7 +455,7 @@ void attn_mfma_kernel(AttnArgs a) {
         // Exact step: the row maximum of the stage (a tree of three-input
         // maxima, then the lane pair), the running maximum raised to it, and
         // the running sum and output rescaled by exp2(old - new).
-        auto raise_max = [&]() {
+        auto stage_max = [&]() -> float {
             float mk[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
@@ -466,7 +467,9 @@ void attn_mfma_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int kt = 1; kt < NKT; ++kt) mk[0] = fmaxf(mk[0], mk[kt]);
-            const float m_new = fmaxf(m_run, pair_max32(mk[0]) * sl2);
+            return pair_max32(mk[0]) * sl2;
+        };
+        auto rescale = [&](float m_new) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
             m_run = m_new;
             l_run *= alpha;
@@ -475,6 +478,7 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         };
+        auto raise_max = [&]() { rescale(fmaxf(m_run, stage_max())); };
         // The running maximum is only raised when it must be.  A row's first
         // live stage takes the exact step.  Later stages exponentiate against
         // the current maximum and check the lane's stage sum: at most kSumCap
@@ -483,8 +487,16 @@ void attn_mfma_kernel(AttnArgs a) {
         // scale) keeps the values, otherwise (a score far above the running
         // maximum, an overflow to inf included) the stage takes the exact step
         // and exponentiates again.  Each branch is wave-uniform.
+        // The key-mask variant takes the exact step on every stage (raising
+        // the maximum only when it grows by more than 2^kTau): holding S for a
+        // second pass would cost it a workgroup per CU at D = 64.
         float ps;
-        if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
+        if constexpr (KMASK) {
+            const float mx = stage_max();
+            const bool grow = mx > m_run + kTau;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale(grow ? mx : m_run);   // wave-uniform
+            ps = make_p();
+        } else if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
             raise_max();
             ps = make_p();
         } else {

@@ -168,7 +168,10 @@ void attn_mfma_kernel(AttnArgs a) {
     static_assert((TILE * 2) % (D * 2) == 0, "tiles hold whole rows");
 
     const int64_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (a.head_mask == nullptr && L >= a.n_work) return;
+    // the grid is padded to a multiple of the XCD count: padding workgroups
+    // exit here (SHARE: one workgroup per pair of query heads, so half the
+    // (b, head, query block) items)
+    if (a.head_mask == nullptr && L >= (SHARE ? a.n_work / 2 : a.n_work)) return;
     // work order (b, kv head, query block, query head within the group): the
     // query heads that share one K/V head run the same query block on
     // neighbouring workgroups of one XCD, so their K/V tiles meet in its L2

@@ -80,3 +80,28 @@ def test_per_head_fallbacks(cuda):
     per_head = (rng.random((1, 4, nb, nb)) < 0.5).astype(np.uint8)
     got = run(cuda, q, k, v, per_head)
     assert_close(got, oracle.attention(to64(q), to64(k), to64(v), 64, per_head), "bf16", "per-head masks")
+
+
+@pytest.mark.parametrize("D,nb", [(128, 10), (64, 9)])
+@pytest.mark.parametrize("masked", [False, True], ids=["plain", "key_mask"])
+def test_padded_grid_stays_in_bounds(cuda, D, nb, masked):
+    # B 1, four query heads on two K/V heads: nb * 2 shared-tile workgroups
+    # (20 or 18), a grid padded to 24.  The padding workgroups must exit
+    # without touching memory: Q, K, V and O are batch 0 of two-batch
+    # buffers, and the output buffer's second batch must keep its fill.
+    B, H, Hkv, N = 1, 4, 2, nb * 64
+    q, k, v = workloads.small_case(B=B, H=H, Hkv=Hkv, N=N, D=D, seed=97)
+    bufs = []
+    for t in (q, k, v):
+        big = torch.zeros((2,) + tuple(t.shape[1:]), dtype=t.dtype, device=cuda)
+        big[:1].copy_(t.to(cuda))
+        bufs.append(big[:1])
+    out_big = torch.full((2, H, N, D), 7.0, dtype=torch.bfloat16, device=cuda)
+    mask = np.ones((1, 1, nb, nb), np.uint8)
+    km = np.ones((1, N), np.uint8) if masked else None
+    hm.forward(*bufs, upload_mask(mask, cuda), out=out_big[:1],
+               key_mask=None if km is None else torch.from_numpy(km).to(cuda))
+    torch.cuda.synchronize()
+    assert bool(torch.all(out_big[1] == 7.0))
+    ref = oracle.attention(to64(q), to64(k), to64(v), 64, mask, key_mask=km)
+    assert_close(to64(out_big[:1]), ref, "bf16", f"padded grid D{D} nb{nb}")

@@ -244,3 +244,35 @@ def test_padding_contents_do_not_reach_live_rows(cuda):
     live = torch.cat([torch.arange(0, 128), torch.arange(512, w.N)]).to(cuda)
     assert torch.equal(a[:, :, live], b[:, :, live])
     assert torch.all(b[:, :, 128:512] == 0)
+
+
+GROWING = [
+    # (name, H, Hkv, D, step, jump_block, jump)
+    ("d64_steps", 2, 2, 64, 2.0, None, 0.0),
+    ("d128_steps", 2, 2, 128, 1.5, None, 0.0),
+    ("d64_overflow_jump", 2, 2, 64, 0.5, 6, 25.0),
+    ("d128_gqa_shared_overflow_jump", 4, 2, 128, 1.0, 5, 30.0),
+]
+
+
+@pytest.mark.parametrize("case", GROWING, ids=[g[0] for g in GROWING])
+@pytest.mark.parametrize("masked", [False, True], ids=["plain", "key_mask"])
+def test_forward_steeply_growing_scores(cuda, case, masked):
+    # Scores rise by tens of log2 units from one key block to the next (and by
+    # hundreds at the jump, where exponentials against the old row maximum
+    # overflow fp32), so the online softmax must raise a row's running maximum
+    # on stages after its first one; the alternate rows' scores fall instead.
+    # Every block is kept, in ascending order, in one mask shared by all heads.
+    name, H, Hkv, D, step, jump_block, jump = case
+    nb = 10
+    q, k, v = workloads.growing_scores_case(B=1, H=H, Hkv=Hkv, nb=nb, D=D, step=step,
+                                            jump_block=jump_block, jump=jump, seed=31)
+    mask = np.ones((1, 1, nb, nb), np.uint8)
+    km = np.ones((1, nb * 64), np.uint8) if masked else None
+    out = hm.forward(q.to(cuda), k.to(cuda), v.to(cuda), upload_mask(mask, cuda),
+                     key_mask=None if km is None else torch.from_numpy(km).to(cuda))
+    torch.cuda.synchronize()
+    ref = oracle.attention(to64(q), to64(k), to64(v), 64, mask, key_mask=km)
+    got = to64(out)
+    assert np.all(np.isfinite(got))
+    assert_close(got, ref, "bf16", f"growing scores {name} {'key mask' if masked else 'plain'}")

@@ -155,6 +155,27 @@ def small_case(B=1, H=2, Hkv=None, N=512, D=64, block=64, dtype="bf16", seed=0, 
     return q.to(dt).to(device), k.to(dt).to(device), v.to(dt).to(device)
 
 
+def growing_scores_case(B=1, H=2, Hkv=None, nb=10, D=64, step=2.0, jump_block=None, jump=0.0, seed=0):
+    """bf16 Q/K/V (block 64) whose scores change steeply from one key block to
+    the next: every query row is +-(1 + N(0, 0.05)) in all D entries (the sign
+    alternates by row), and every key of block j is s_j + N(0, 0.1) in all
+    entries, with s_j = step * j, plus `jump` from block `jump_block` on.  For
+    the +1 rows a score grows by about D * step per key block (the -1 rows
+    shrink); V is iid N(0, 1).  Used to drive the online softmax through large
+    increases of a row's maximum, up to exponentials that overflow fp32."""
+    Hkv = Hkv or H
+    N = nb * 64
+    g = torch.Generator().manual_seed(seed)
+    sign = torch.where(torch.arange(N) % 2 == 0, 1.0, -1.0)
+    q = sign[None, None, :, None] * (1.0 + 0.05 * torch.randn((B, H, N, D), generator=g))
+    level = step * (torch.arange(N) // 64).to(torch.float32)
+    if jump_block is not None:
+        level = level + jump * (torch.arange(N) // 64 >= jump_block).to(torch.float32)
+    k = level[None, None, :, None] + 0.1 * torch.randn((B, Hkv, N, D), generator=g)
+    v = torch.randn((B, Hkv, N, D), generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 def random_head_mask(H: int, seed: int) -> np.ndarray:
     """A random 0/1 head mask with at least one active head (test input)."""
     rng = np.random.default_rng(seed)

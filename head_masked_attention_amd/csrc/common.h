@@ -19,6 +19,7 @@ enum BlockClass : int32_t { CLS_SPARSE = 0, CLS_PINNED = 1, CLS_DROPPED = 2 };
 
 constexpr int kMaxRuns = 72;      // class runs; <= 2 * BSATTN_MAX_SEGMENTS + 1 in practice
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int64_t kL2BytesPerXcd = 4 << 20;   // MI355X: 4 MB of L2 per XCD
 constexpr int kMaxCand = 2048;    // sparsifiable blocks handled by the selector
 
 // Rows per (b, head) of the pooled sums in the selector workspace: the

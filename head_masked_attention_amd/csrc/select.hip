@@ -66,10 +66,16 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
 // Ranking by <sum Q_i, sum K_j> equals ranking by the mean-pooled score: the
 // factor 1/block^2 is a positive constant.
 // ---------------------------------------------------------------------------
+// xcd_groups: items in (b, K/V head) groups -- the query heads of the group,
+// then the K/V head -- in the XCD-grouped workgroup order of the attention
+// kernel, so that the XCD that pools a group's Q and K is the one whose
+// attention workgroups read them next, from its L2 when an XCD's share fits
+// there (the host decides).  Otherwise the plain order (tensor, b, head,
+// block).
 template <typename T, int D, int BLOCK>
 __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int H, int Hkv,
                                                    Geometry g, float* __restrict__ qp,
-                                                   float* __restrict__ kp) {
+                                                   float* __restrict__ kp, int xcd_groups) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per token row
     constexpr int RPI = 64 / CPR;              // token rows per wave instruction
@@ -77,20 +83,34 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     static_assert(CPR <= 64 && 64 % CPR == 0 && BLOCK % RPI == 0, "pool geometry");
 
     const int lane = threadIdx.x & 63;
-    // wave-uniform, so that the run lookup below is scalar
-    const int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: scalar lookups
     const int64_t nq = (int64_t)B * H * g.n_cand;
     const int64_t nk = (int64_t)B * Hkv * g.n_cand;
-    if (item >= nq + nk) return;
-
     const TView* src;
-    int64_t rem, heads;
+    int64_t hh, b, p, heads;
     float* out;
-    if (item < nq) { src = &q; rem = item; heads = H; out = qp; }
-    else { src = &k; rem = item - nq; heads = Hkv; out = kp; }
-    const int64_t p = rem % g.n_cand;
-    const int64_t hh = (rem / g.n_cand) % heads;
-    const int64_t b = rem / (g.n_cand * heads);
+    if (xcd_groups) {
+        const int64_t item = xcd_logical_id(blockIdx.x, gridDim.x) * 4 + wave;   // grid: a multiple of 8
+        if (item >= nq + nk) return;
+        const int64_t rep = H / Hkv;
+        const int64_t per_group = (rep + 1) * g.n_cand;
+        const int64_t grp = item / per_group, r = item % per_group;
+        b = grp / Hkv;
+        if (r < rep * g.n_cand) {
+            src = &q; heads = H; out = qp; hh = (grp % Hkv) * rep + r / g.n_cand; p = r % g.n_cand;
+        } else {
+            src = &k; heads = Hkv; out = kp; hh = grp % Hkv; p = r - rep * g.n_cand;
+        }
+    } else {
+        const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+        if (item >= nq + nk) return;
+        int64_t rem;
+        if (item < nq) { src = &q; rem = item; heads = H; out = qp; }
+        else { src = &k; rem = item - nq; heads = Hkv; out = kp; }
+        p = rem % g.n_cand;
+        hh = (rem / g.n_cand) % heads;
+        b = rem / (g.n_cand * heads);
+    }
     const int64_t blk = cand_block(g, (int32_t)p);
     float* dst = out + (b * heads + hh) * (int64_t)pooled_rows(g.n_cand) * D;
 
@@ -543,9 +563,14 @@ template <typename T, int D>
 static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
                                 const Geometry& g, float* qp, float* kp, hipStream_t s) {
     const int64_t items = (int64_t)B * (H + Hkv) * g.n_cand;
-    const dim3 grid((unsigned)((items + 3) / 4));
-    if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp);
-    return launch(pool_kernel<T, D, 32>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp);
+    // the XCD-grouped order when an XCD's share of the pooled Q and K fits in
+    // its L2 (4 MB), where the attention launch that follows can find it
+    const int64_t bytes = items * block * D * (int64_t)sizeof(T);
+    const int xcd_groups = bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
+    const int64_t wgs = (items + 3) / 4;
+    const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
+    if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
+    return launch(pool_kernel<T, D, 32>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
 }
 
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,

@@ -212,6 +212,8 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
     Geometry g;
     if ((st = make_geometry(layout, q->N, budget, g)) != BSATTN_OK) return st;
     if (!g.is_dense && g.n_cand > kMaxCand) return BSATTN_ERR_UNSUPPORTED;
+    // the pool kernel indexes its (tensor, b, head, candidate) items in 32 bits
+    if (!g.is_dense && q->B * (q->H + k->H) * g.n_cand > INT32_MAX) return BSATTN_ERR_SHAPE;
     const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, layout->block, q->D);
     if (!g.is_dense) {
         if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;

@@ -83,43 +83,57 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     static_assert(CPR <= 64 && 64 % CPR == 0 && BLOCK % RPI == 0, "pool geometry");
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: scalar lookups
-    const int64_t nq = (int64_t)B * H * g.n_cand;
-    const int64_t nk = (int64_t)B * Hkv * g.n_cand;
-    const TView* src;
-    int64_t hh, b, p, heads;
-    float* out;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: scalar lookups
+    // 32-bit index arithmetic (the host checks that the items fit): the
+    // division sequences sit in front of every wavefront's loads
+    const uint32_t nc = (uint32_t)g.n_cand;
+    const uint32_t nq = (uint32_t)B * (uint32_t)H * nc, nk = (uint32_t)B * (uint32_t)Hkv * nc;
+    // which tensor, (b, head) and candidate this wavefront pools; the
+    // tensor's fields are selected by value (a pointer to a kernel argument
+    // would put both views in scratch memory)
+    bool is_q;
+    uint32_t hh, b, p;
     if (xcd_groups) {
-        const int64_t item = xcd_logical_id(blockIdx.x, gridDim.x) * 4 + wave;   // grid: a multiple of 8
+        const uint32_t item = (uint32_t)xcd_logical_id(blockIdx.x, gridDim.x) * 4u + wave;   // grid: a multiple of 8
         if (item >= nq + nk) return;
-        const int64_t rep = H / Hkv;
-        const int64_t per_group = (rep + 1) * g.n_cand;
-        const int64_t grp = item / per_group, r = item % per_group;
-        b = grp / Hkv;
-        if (r < rep * g.n_cand) {
-            src = &q; heads = H; out = qp; hh = (grp % Hkv) * rep + r / g.n_cand; p = r % g.n_cand;
+        const uint32_t rep = (uint32_t)(H / Hkv);
+        const uint32_t per_group = (rep + 1) * nc;
+        const uint32_t grp = item / per_group, r = item - grp * per_group;
+        b = grp / (uint32_t)Hkv;
+        const uint32_t kvh = grp - b * (uint32_t)Hkv;
+        is_q = r < rep * nc;
+        if (is_q) {
+            const uint32_t j = r / nc;
+            hh = kvh * rep + j;
+            p = r - j * nc;
         } else {
-            src = &k; heads = Hkv; out = kp; hh = grp % Hkv; p = r - rep * g.n_cand;
+            hh = kvh;
+            p = r - rep * nc;
         }
     } else {
-        const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+        const uint32_t item = blockIdx.x * 4u + wave;
         if (item >= nq + nk) return;
-        int64_t rem;
-        if (item < nq) { src = &q; rem = item; heads = H; out = qp; }
-        else { src = &k; rem = item - nq; heads = Hkv; out = kp; }
-        p = rem % g.n_cand;
-        hh = (rem / g.n_cand) % heads;
-        b = rem / (g.n_cand * heads);
+        is_q = item < nq;
+        const uint32_t rem = is_q ? item : item - nq;
+        const uint32_t heads = is_q ? (uint32_t)H : (uint32_t)Hkv;
+        const uint32_t bh = rem / nc;
+        p = rem - bh * nc;
+        b = bh / heads;
+        hh = bh - b * heads;
     }
-    const int64_t blk = cand_block(g, (int32_t)p);
-    float* dst = out + (b * heads + hh) * (int64_t)pooled_rows(g.n_cand) * D;
+    const T* src_p = (const T*)(is_q ? q.p : k.p);
+    const int64_t sb = is_q ? q.sb : k.sb, sh = is_q ? q.sh : k.sh, sn = is_q ? q.sn : k.sn;
+    const int64_t heads = is_q ? H : Hkv;
+    float* out = is_q ? qp : kp;
 
-    const T* base = (const T*)src->p + b * src->sb + hh * src->sh +
-                    (blk * BLOCK + lane / CPR) * src->sn + (lane % CPR) * EPC;
+    const int64_t blk = cand_block(g, (int32_t)p);
+    float* dst = out + ((int64_t)b * heads + hh) * pooled_rows(g.n_cand) * D;
+
+    const T* base = src_p + b * sb + hh * sh + (blk * BLOCK + lane / CPR) * sn + (lane % CPR) * EPC;
     uint4 raw[NL];
 #pragma unroll
     for (int l = 0; l < NL; ++l)
-        raw[l] = *(const uint4*)(base + (int64_t)l * RPI * src->sn);
+        raw[l] = *(const uint4*)(base + (int64_t)l * RPI * sn);
 
     float acc[EPC];
 #pragma unroll

@@ -164,6 +164,17 @@ def test_select_unsupported_candidate_count(lib):
     assert call_select(lib, q, k, lay, 0.3, bmask(nb=2100)) == 9
 
 
+def test_select_item_count_limit(lib):
+    # the pool kernel indexes B * (H + Hkv) * n_cand items in 32 bits
+    B, H, N = 1 << 20, 1024, 64 * 64
+    q, k = tensor(B=B, H=H, N=N), tensor(B=B, H=H, N=N)
+    lay, _k = layout()
+    assert call_select(lib, q, k, lay, 0.3, bmask(B=B, H=H, nb=64)) == 3
+    B = 1 << 8                                          # 2^8 * 2048 * 64 items pass; the 1 GiB workspace is too small
+    q, k = tensor(B=B, H=H, N=N), tensor(B=B, H=H, N=N)
+    assert call_select(lib, q, k, lay, 0.3, bmask(B=B, H=H, nb=64)) == 7
+
+
 def call_forward(lib, q, k, v, m, out, scale=0.0):
     return lib.bsattn_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                               None if m is None else ctypes.byref(m), None, scale,

@@ -230,10 +230,15 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
     } else {
         float* qp = (float*)workspace;
         float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
+        // the XCD-grouped order when an XCD's share of the pooled Q and K fits
+        // in its L2, where the attention launch that follows finds it
+        const int64_t pooled_bytes = q->B * (q->H + k->H) * g.n_cand * layout->block * q->D *
+                                     (q->dtype == BSATTN_F32 ? 4 : 2);
+        const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
         e = launch_pool(q->dtype == BSATTN_F32, (int)q->D, layout->block, view_of(q), view_of(k),
-                        (int)q->B, (int)q->H, (int)k->H, g, qp, kp, s);
+                        (int)q->B, (int)q->H, (int)k->H, g, qp, kp, xcd_groups, s);
         if (e == hipSuccess)
-            e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, s);
+            e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, xcd_groups, s);
     }
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }

@@ -21,10 +21,14 @@ struct AttnArgs {
     int64_t n_work;              // B * H * nqb workgroups of real work
 };
 
+// xcd_groups: the selector's two launches take their work in the attention
+// kernel's XCD-grouped (b, K/V head) order, so that pooled sums, masks and
+// lists are written by the XCD whose attention workgroups read them next
+// (chosen by the host when an XCD's share of Q and K fits in its L2).
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, float* qp, float* kp, hipStream_t s);
+                       int Hkv, const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s);
 hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
-                             const Geometry& g, MaskOut out, hipStream_t s);
+                             const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s);
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
 
 // bf16, block 64, D in {64, 128}: MFMA path.

@@ -365,7 +365,7 @@ struct RankShape {
 template <int D, int E>
 __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, int B, int H, int Hkv, Geometry g,
-    MaskOut out, int n_tiles) {
+    MaskOut out, int n_tiles, int xcd_groups) {
     constexpr int NPAD = 64 * E;
     constexpr int RT = RankShape<E>::RT;
     constexpr int WAVES = RankShape<E>::WAVES;
@@ -383,8 +383,12 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     const bool vec4 = (g.nb & 3) == 0 && ((uintptr_t)out.mask & 3u) == 0;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x % n_tiles;
-    const int64_t bh = blockIdx.x / n_tiles;
+    // xcd_groups: the (b, head, tile) order of the XCD-grouped workgroup ids
+    // (the grid is then padded to a multiple of 8)
+    const int64_t wg = xcd_groups ? xcd_logical_id(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+    if (wg >= (int64_t)B * H * n_tiles) return;
+    const int tile = (int)(wg % n_tiles);
+    const int64_t bh = wg / n_tiles;
     const int64_t b = bh / H, h = bh % H;
     const int64_t g_kv = h / (H / Hkv);
     const int p0 = tile * RT;
@@ -575,12 +579,8 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
-                                const Geometry& g, float* qp, float* kp, hipStream_t s) {
+                                const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s) {
     const int64_t items = (int64_t)B * (H + Hkv) * g.n_cand;
-    // the XCD-grouped order when an XCD's share of the pooled Q and K fits in
-    // its L2 (4 MB), where the attention launch that follows can find it
-    const int64_t bytes = items * block * D * (int64_t)sizeof(T);
-    const int xcd_groups = bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
     const int64_t wgs = (items + 3) / 4;
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
     if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
@@ -588,44 +588,45 @@ static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int H
 }
 
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, float* qp, float* kp, hipStream_t s) {
+                       int Hkv, const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s) {
     if (dtype_is_f32) {
-        if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, s);
-        if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, s);
-        return launch_pool_t<float, 128>(block, q, k, B, H, Hkv, g, qp, kp, s);
+        if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+        if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+        return launch_pool_t<float, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
     }
-    if (D == 32) return launch_pool_t<uint16_t, 32>(block, q, k, B, H, Hkv, g, qp, kp, s);
-    if (D == 64) return launch_pool_t<uint16_t, 64>(block, q, k, B, H, Hkv, g, qp, kp, s);
-    return launch_pool_t<uint16_t, 128>(block, q, k, B, H, Hkv, g, qp, kp, s);
+    if (D == 32) return launch_pool_t<uint16_t, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+    if (D == 64) return launch_pool_t<uint16_t, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+    return launch_pool_t<uint16_t, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
 }
 
 template <int D, int E>
 static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H, int Hkv,
-                                 const Geometry& g, MaskOut out, hipStream_t s) {
+                                 const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
     constexpr int RT = RankShape<E>::RT;
     const int n_tiles = (g.n_cand + RT - 1) / RT;
-    const dim3 grid((unsigned)((int64_t)B * H * n_tiles));
+    const int64_t wgs = (int64_t)B * H * n_tiles;
+    const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
     return launch(score_rank_kernel<D, E>, grid, dim3(RankShape<E>::WAVES * 64), s, qp, kp, B, H, Hkv, g,
-                  out, n_tiles);
+                  out, n_tiles, xcd_groups);
 }
 
 template <int D>
 static hipError_t launch_score_d(const float* qp, const float* kp, int B, int H, int Hkv,
-                                 const Geometry& g, MaskOut out, hipStream_t s) {
+                                 const Geometry& g, MaskOut out, int xg, hipStream_t s) {
     const int n = g.n_cand;
-    if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, s);
-    if (n <= 128) return launch_score_t<D, 2>(qp, kp, B, H, Hkv, g, out, s);
-    if (n <= 256) return launch_score_t<D, 4>(qp, kp, B, H, Hkv, g, out, s);
-    if (n <= 512) return launch_score_t<D, 8>(qp, kp, B, H, Hkv, g, out, s);
-    if (n <= 1024) return launch_score_t<D, 16>(qp, kp, B, H, Hkv, g, out, s);
-    return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, s);
+    if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, xg, s);
+    if (n <= 128) return launch_score_t<D, 2>(qp, kp, B, H, Hkv, g, out, xg, s);
+    if (n <= 256) return launch_score_t<D, 4>(qp, kp, B, H, Hkv, g, out, xg, s);
+    if (n <= 512) return launch_score_t<D, 8>(qp, kp, B, H, Hkv, g, out, xg, s);
+    if (n <= 1024) return launch_score_t<D, 16>(qp, kp, B, H, Hkv, g, out, xg, s);
+    return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, xg, s);
 }
 
 hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
-                             const Geometry& g, MaskOut out, hipStream_t s) {
-    if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, s);
-    if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, s);
-    return launch_score_d<128>(qp, kp, B, H, Hkv, g, out, s);
+                             const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
+    if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
+    if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
+    return launch_score_d<128>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
 }
 
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s) {

@@ -335,18 +335,26 @@ __device__ __forceinline__ void wave_bitonic_desc32(uint32_t (&key)[R][E], int l
 // Rows per workgroup and wavefronts per workgroup of the score/rank kernel:
 // one 16-row MFMA tile per workgroup (more workgroups beat longer ones:
 // 32-row tiles took 32 -> 26 us on the joint text+image shape and 100 -> 70 us
-// on the video shape).  Up to 128 candidates each wavefront ranks and
-// compacts one row; the compaction of a row is a few hundred dependent scalar
-// and vector instructions, so rows compact side by side rather than one after
-// another.  Longer rows are ranked two at a time by one wavefront, whose
-// interleaved sorting networks hide each other's exchange latency.
+// on the video shape).  Up to 128 candidates each wavefront ranks one row:
+// the compaction of a row is a few hundred scalar and vector instructions,
+// so rows compact side by side rather than one after another.  At D <= 64
+// four workgroups share a tile -- each computes the (small) tile and ranks
+// four of its rows -- spreading the rows over more CUs with fewer
+// wavefronts per SIMD (SDXL shape 9.4 -> 8.8 us); at D = 128 one workgroup
+// of 16 wavefronts takes the tile (a split would reload 32 KB of key sums per
+// workgroup: 64-layer stack 18.6 -> 20.6 us).  Longer rows are ranked two at a
+// time by one wavefront, whose interleaved sorting networks hide each other's
+// exchange latency.
 #ifndef BSATTN_RANK_ONE_ROW_EMAX
 #define BSATTN_RANK_ONE_ROW_EMAX 2
 #endif
-template <int E>
+template <int D, int E>
 struct RankShape {
-    static constexpr int RT = 16;
-    static constexpr int WAVES = E <= BSATTN_RANK_ONE_ROW_EMAX ? 16 : 8;
+    static constexpr bool SHORT = E <= BSATTN_RANK_ONE_ROW_EMAX;
+    static constexpr bool SPLIT = SHORT && D <= 64;   // at D = 128 each split reloads 32 KB of key sums
+    static constexpr int RT = 16;                       // rows of the score MFMA tile
+    static constexpr int RQ = SPLIT ? 4 : 16;           // rows ranked per workgroup
+    static constexpr int WAVES = SPLIT ? 4 : (SHORT ? 16 : 8);
 };
 
 // ---------------------------------------------------------------------------
@@ -363,14 +371,16 @@ struct RankShape {
 // index.  Larger candidate sets use 64-bit keys (full score, then position).
 // ---------------------------------------------------------------------------
 template <int D, int E>
-__global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
+__global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, int B, int H, int Hkv, Geometry g,
     MaskOut out, int n_tiles, int xcd_groups) {
     constexpr int NPAD = 64 * E;
-    constexpr int RT = RankShape<E>::RT;
-    constexpr int WAVES = RankShape<E>::WAVES;
+    constexpr int RT = RankShape<D, E>::RT;
+    constexpr int RQ = RankShape<D, E>::RQ;
+    constexpr int SPLITS = RT / RQ;            // workgroups per tile
+    constexpr int WAVES = RankShape<D, E>::WAVES;
     constexpr bool K32 = E <= 8;
-    constexpr int RPW = RT / WAVES;            // rows per wavefront
+    constexpr int RPW = RQ / WAVES;            // rows per wavefront
     constexpr int RR = RPW >= 2 ? 2 : 1;       // rows ranked together (32-bit keys)
     constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
     constexpr int KQ = D / 4;                  // MFMA k-steps; lane group gq owns d in [gq*KQ, gq*KQ+KQ)
@@ -386,9 +396,10 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     // xcd_groups: the (b, head, tile) order of the XCD-grouped workgroup ids
     // (the grid is then padded to a multiple of 8)
     const int64_t wg = xcd_groups ? xcd_logical_id(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
-    if (wg >= (int64_t)B * H * n_tiles) return;
-    const int tile = (int)(wg % n_tiles);
-    const int64_t bh = wg / n_tiles;
+    if (wg >= (int64_t)B * H * n_tiles * SPLITS) return;
+    const int sub = (int)(wg % SPLITS);        // which RQ rows of the tile this workgroup ranks
+    const int tile = (int)((wg / SPLITS) % n_tiles);
+    const int64_t bh = wg / SPLITS / n_tiles;
     const int64_t b = bh / H, h = bh % H;
     const int64_t g_kv = h / (H / Hkv);
     const int p0 = tile * RT;
@@ -456,7 +467,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
         // ---- RR rows at a time per wavefront
         constexpr int IB = __builtin_ctz(NPAD);            // index bits
         constexpr uint32_t IMASK = (1u << IB) - 1u;
-        for (int r0 = wave * RPW; r0 < wave * RPW + RPW; r0 += RR) {
+        for (int r0 = sub * RQ + wave * RPW; r0 < sub * RQ + wave * RPW + RPW; r0 += RR) {
             uint32_t key[RR][E];
 #pragma unroll
             for (int q = 0; q < RR; ++q) {
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
         }
     } else {
         // ---- 64-bit keys, one row at a time
-        for (int rl = wave * RPW; rl < wave * RPW + RPW; ++rl) {
+        for (int rl = sub * RQ + wave * RPW; rl < sub * RQ + wave * RPW + RPW; ++rl) {
             if (rl >= rows) break;
             const int p = p0 + rl;
             uint64_t key[E];
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(RankShape<E>::WAVES * 64) void score_rank_kernel(
     }
 
     // ---- this workgroup's share of the PINNED and DROPPED rows
-    for (int t = tile * WAVES + wave; t < g.n_other; t += n_tiles * WAVES) {
+    for (int t = (tile * SPLITS + sub) * WAVES + wave; t < g.n_other; t += n_tiles * SPLITS * WAVES) {
         const int32_t i = other_block(g, t);
         const int32_t cls = block_class(g, i);
         compact_row(g, codes, vec4, lane, cls == CLS_DROPPED, cls == CLS_PINNED,
@@ -602,11 +613,11 @@ hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int
 template <int D, int E>
 static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H, int Hkv,
                                  const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
-    constexpr int RT = RankShape<E>::RT;
+    constexpr int RT = RankShape<D, E>::RT;
     const int n_tiles = (g.n_cand + RT - 1) / RT;
-    const int64_t wgs = (int64_t)B * H * n_tiles;
+    const int64_t wgs = (int64_t)B * H * n_tiles * (RT / RankShape<D, E>::RQ);
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
-    return launch(score_rank_kernel<D, E>, grid, dim3(RankShape<E>::WAVES * 64), s, qp, kp, B, H, Hkv, g,
+    return launch(score_rank_kernel<D, E>, grid, dim3(RankShape<D, E>::WAVES * 64), s, qp, kp, B, H, Hkv, g,
                   out, n_tiles, xcd_groups);
 }
 

@@ -36,6 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 ATTN_SOURCES = ["head_masked_attention_amd/csrc/attn_mfma.hip", "head_masked_attention_amd/csrc/common.h",
+                "head_masked_attention_amd/csrc/rank.h",
                 "head_masked_attention_amd/csrc/internal.h"]
 
 
@@ -79,6 +80,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--two-calls", action="store_true",
+                   help="run the step as bsattn_select + bsattn_forward even where bsattn_select_forward "
+                        "fuses the ranking into the attention kernel")
     p.add_argument("--graph", action="store_true",
                    help="replay the step (and the per-call loops) as captured HIP graphs instead of "
                         "launching every call from the host")
@@ -270,10 +274,29 @@ def main():
         ly = layers[i]
         hm.forward(ly["qd"], ly["kd"], ly["vd"], bms[i] if bm is None else bm, ly["hmd"], out=outs[i], stream=st)
 
-    def step(st):
+    def select_forward(i, st):
+        ly = layers[i]
+        hm.select_forward(ly["qd"], ly["kd"], ly["vd"], layout, w.budget, ly["hmd"], out=outs[i],
+                          block_mask=bms[i], workspace=ws, stream=st)
+
+    def two_call_step(st):
         for i in range(L):
             select(i, st)
             forward(i, st)
+
+    # The step is bsattn_select_forward: the same selection and attention,
+    # with the ranking inside the attention kernel where that kernel applies
+    # (bf16, D 64, block 64, every block a candidate, at most 64 blocks, no
+    # head mask), else the two calls.
+    fused = (not args.two_calls and w.dtype == "bf16" and w.D == 64 and w.block == 64 and not w.segments
+             and not w.window_tokens and w.nb <= 64 and w.budget < 1.0 and all(ly["hmd"] is None for ly in layers))
+
+    def step(st):
+        if not fused:
+            two_call_step(st)
+            return
+        for i in range(L):
+            select_forward(i, st)
 
     # ---- whole-step throughput: K steps on the host clock, synchronised on
     # both sides.  Every call is launched from the host (the host runs ahead
@@ -303,6 +326,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    two_call_ms = None
+    if fused and not args.graph:
+        # the same step as bsattn_select + bsattn_forward, for reference
+        for _ in range(args.warmup):
+            two_call_step(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            two_call_step(stream)
+        torch.cuda.synchronize()
+        two_call_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # ---- per-call figures (layer 0), warm: back-to-back calls in one graph
     reps = max(1, min(args.steps, 50))
@@ -425,6 +459,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; clustered Q/K for image workloads)",
         "step_launch": "hip graph replay" if args.graph else "host launches",
+        "step_calls": "bsattn_select_forward (ranking fused into the attention kernel)" if fused
+                      else "bsattn_select + bsattn_forward",
+        "two_call_ms_per_step": two_call_ms,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
                    "block": w.block, "budget": w.budget, "k": bms[0].k,
                    "layers": L, "layer": layer_ids[0] if L == 1 else None,

@@ -60,7 +60,7 @@ class _BlockMask(ctypes.Structure):
 EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_select_workspace_bytes", "bsattn_select", "bsattn_radial", "bsattn_forward",
            "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8", "bsattn_forward_fp8_masked",
-           "bsattn_head_mask", "bsattn_mask_density",
+           "bsattn_head_mask", "bsattn_mask_density", "bsattn_select_forward",
            "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
            "bsattn_stage_outcome_string"]
 
@@ -109,6 +109,9 @@ def load_library(path: str = LIB_PATH):
                                   ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P,
                                   ctypes.c_size_t, P]
     lib.bsattn_radial.argtypes = [ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
+    lib.bsattn_select_forward.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                          ctypes.POINTER(_Layout), dbl, P, ctypes.c_float, ctypes.POINTER(_Tensor),
+                                          ctypes.POINTER(_BlockMask), P, ctypes.c_size_t, P]
     lib.bsattn_forward.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                    ctypes.POINTER(_Tensor), ctypes.POINTER(_BlockMask), P,
                                    ctypes.c_float, ctypes.POINTER(_Tensor), P]
@@ -238,6 +241,37 @@ def select(q, k, layout: Layout, budget: float, *, out: BlockMask | None = None,
     _check(st, "bsattn_select")
     out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
     return out
+
+
+def select_forward(q, k, v, layout: Layout, budget: float, head_mask=None, scale: float = 0.0, *,
+                   out=None, block_mask: BlockMask | None = None, workspace=None, stream=None):
+    """bsattn_select_forward: selection and attention in one call (the result
+    of select followed by forward).  Returns (out, block_mask)."""
+    import torch
+    lib = load_library()
+    B, H, N, D = q.shape
+    nb = N // layout.block
+    if block_mask is None:
+        block_mask = empty_block_mask(B, H, nb, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    need = select_workspace_bytes(B, H, k.shape[1], N, layout.block, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    hm_ptr = None
+    if head_mask is not None:
+        if head_mask.dtype != torch.uint8 or not head_mask.is_cuda or head_mask.numel() != H:
+            raise BsattnError(3, "bsattn_select_forward", "head_mask must be a uint8 device tensor of H entries")
+        hm_ptr = head_mask.data_ptr()
+    tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    lay, _keep = layout._c()
+    bm = block_mask._c()
+    st = lib.bsattn_select_forward(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(lay),
+                                   float(budget), hm_ptr, float(scale), ctypes.byref(to), ctypes.byref(bm),
+                                   workspace.data_ptr(), workspace.numel(), _stream(q.device, stream))
+    _check(st, "bsattn_select_forward")
+    block_mask.is_dense, block_mask.k = bool(bm.is_dense), int(bm.k)
+    return out, block_mask
 
 
 def radial(layout: Layout, N: int, density: float, *, B: int = 1, H: int = 1, device=None,

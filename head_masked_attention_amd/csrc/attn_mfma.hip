@@ -35,6 +35,7 @@
 // per-layer mask).
 #include "common.h"
 #include "internal.h"
+#include "rank.h"
 
 // 1: workgroups of the query heads sharing a K/V head are neighbours
 #ifndef BSATTN_GQA_ORDER
@@ -135,7 +136,58 @@ enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 // instead of two key-block groups.  They walk the same kept list, so each
 // K/V stage tile is loaded into LDS once (by all four wavefronts) and read
 // by both heads; there is no merge, each pair writes its own head.
-template <int D, int KT, int SPLIT, int WPE, int BUF, bool KMASK, bool SHARE>
+// FUSED (bsattn_select_forward; D 64, every block of the sequence a candidate,
+// at most 64 of them): wavefront 0 ranks the workgroup's row from the
+// selector's pooled sums -- the same 32-bit keys and wavefront bitonic sort
+// as the selector's ranking: the diagonal first, then by score with ties to
+// the lower block, truncated to 2^-14 relative -- keeps the top `keep`,
+// writes the row's mask, count and ascending index list, and leaves the list
+// in LDS for the stage loop.
+__device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, int kvh, int qb, int lane,
+                                               int32_t* s_list, uint8_t* s_flag) {
+    constexpr uint32_t IMASK = 63u;           // 64 candidate positions
+    const int n = a.nkb;
+    const float* qrow = a.qp + ((int64_t)b * a.H + h) * a.prow * 64;
+    const float* krow = a.kp + ((int64_t)b * a.Hkv + kvh) * a.prow * 64;
+    uint32_t key[1][1] = {{0u}};
+    if (lane < n) {
+        if (lane == qb) {
+            key[0][0] = (0xffffffffu & ~IMASK) | (IMASK - (uint32_t)lane);
+        } else {
+            float sc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float4 q4 = *(const float4*)(qrow + pooled_offset<64>(qb, 4 * m));
+                const float4 k4 = *(const float4*)(krow + pooled_offset<64>(lane, 4 * m));
+                sc = fmaf(q4.x, k4.x, sc);
+                sc = fmaf(q4.y, k4.y, sc);
+                sc = fmaf(q4.z, k4.z, sc);
+                sc = fmaf(q4.w, k4.w, sc);
+            }
+            key[0][0] = (orderable(sc) & ~IMASK) | (IMASK - (uint32_t)lane);
+        }
+    }
+    wave_bitonic_desc32<1, 1>(key, lane);          // lane r: the key of rank r
+    s_flag[lane] = 0;
+    s_list[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < a.keep) s_flag[IMASK - (key[0][0] & IMASK)] = 1;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const bool kept = lane < n && s_flag[lane] != 0;
+    const uint64_t bal = __ballot(kept);
+    const int slot = __popcll(bal & ((1ull << lane) - 1ull));
+    if (kept) s_list[slot] = lane;
+    if (a.m_out != nullptr) {
+        const int64_t row = ((int64_t)b * a.H + h) * a.nqb + qb;
+        if (lane < n) a.m_out[row * n + lane] = kept ? 1 : 0;
+        if (kept) a.i_out[row * n + slot] = lane;
+        if (lane == 0) a.c_out[row] = __popcll(bal);
+    }
+}
+
+template <int D, int KT, int SPLIT, int WPE, int BUF, bool KMASK, bool SHARE, bool FUSED = false>
 __global__ __launch_bounds__(128 * SPLIT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_mfma_kernel(AttnArgs a) {
     constexpr int BLK = 64;
@@ -157,6 +209,7 @@ void attn_mfma_kernel(AttnArgs a) {
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key-block groups");
     static_assert(SPLIT == 1 || SPLIT * TILE * 2 >= D * 128, "merge buffer fits in one stage object");
     static_assert(!KMASK || KT == 32, "key-mask words cover one 32-key stage");
+    static_assert(!FUSED || (D == 64 && !SHARE && !KMASK), "fused selection: D 64, per-head path");
 
     // one LDS object per stage (holding every group's tile): distinct objects
     // let the compiler see that the reads of one stage never alias the loads
@@ -233,6 +286,14 @@ void attn_mfma_kernel(AttnArgs a) {
         // row either way; unused when the group has no block)
         blk0 = ((const __attribute__((address_space(4))) int32_t*)list)[!SHARE && grp < a.nkb ? grp : 0];
     }
+    __shared__ int32_t s_list[FUSED ? 64 : 1];
+    __shared__ uint8_t s_flag[FUSED ? 64 : 1];
+    if constexpr (FUSED) {
+        if (wave == 0) fused_rank_row(a, b, h, kvh, qb, lane, s_list, s_flag);
+        __syncthreads();
+        cnt = a.keep;
+        blk0 = s_list[grp];                  // unused when the group has no block
+    }
     uint16_t* obase = (uint16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qb * BLK * a.o_sn;
 
     if (!active || cnt <= 0) {
@@ -263,6 +324,7 @@ void attn_mfma_kernel(AttnArgs a) {
         (const __attribute__((address_space(4))) int32_t*)list;
     auto block_of = [&](int t) -> int32_t {
         const int i = SHARE ? t / SUB : (t / SUB) * SPLIT + grp;
+        if constexpr (FUSED) return t < SUB ? blk0 : __builtin_amdgcn_readfirstlane(s_list[i]);
         return t < SUB ? blk0 : (list == nullptr ? i : klist[i]);
     };
     // per-thread source offsets of the NI chunks it loads per stage: chunk
@@ -627,6 +689,12 @@ static hipError_t launch_attn_mfma_t(const AttnArgs& a, int D, hipStream_t s) {
     return launch(attn_mfma_kernel<64, KMASK ? 32 : BSATTN_D64_KT, SHARE ? 2 : BSATTN_D64_SPLIT,
                                    KMASK ? BSATTN_D64_KM_WPE : BSATTN_D64_WPE, BSATTN_D64_BUF, KMASK, SHARE>,
                   grid, dim3(128 * (SHARE ? 2 : BSATTN_D64_SPLIT)), s, a);
+}
+
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)attn_grid(a.n_work, false));
+    return launch(attn_mfma_kernel<64, BSATTN_D64_KT, BSATTN_D64_SPLIT, BSATTN_D64_WPE, BSATTN_D64_BUF, false, false, true>,
+                  grid, dim3(128 * BSATTN_D64_SPLIT), s, a);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s) {

@@ -295,7 +295,7 @@ bsattn_status bsattn_forward_fp8_masked(const bsattn_tensor* q, const bsattn_ten
     if (k->stride_n > (1 << 24) || v->stride_n > (1 << 24)) return BSATTN_ERR_UNSUPPORTED;
     if (key_mask != nullptr && (key_mask_stride_b < 0 || (key_mask_stride_b > 0 && key_mask_stride_b < q->N)))
         return BSATTN_ERR_STRIDE;
-    AttnArgs a;
+    AttnArgs a{};
     a.q = view_of(q);
     a.k = view_of(k);
     a.v = view_of(v);
@@ -376,7 +376,7 @@ bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor*
     if (key_mask != nullptr && (key_mask_stride_b < 0 || (key_mask_stride_b > 0 && key_mask_stride_b < q->N)))
         return BSATTN_ERR_STRIDE;
 
-    AttnArgs a;
+    AttnArgs a{};
     a.q = view_of(q);
     a.k = view_of(k);
     a.v = view_of(v);
@@ -408,6 +408,88 @@ bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor*
     }
     else
         e = launch_attn_vec(a, q->dtype == BSATTN_F32, (int)q->D, (int)block, s);
+    return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor* k,
+                                    const bsattn_tensor* v, const bsattn_layout* layout, double budget,
+                                    const uint8_t* head_mask, float scale, bsattn_tensor* out,
+                                    bsattn_block_mask* mask, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || layout == nullptr || out == nullptr || mask == nullptr)
+        return BSATTN_ERR_NULL;
+    // The fused kernel covers the shape where every block of the sequence is
+    // a candidate and a row fits one wavefront: bf16, D 64, block 64, no
+    // layout segments and no window, at most 64 blocks, a selective budget,
+    // no head mask.  Everything else is bsattn_select followed by
+    // bsattn_forward, with identical results.
+    bool fused = q->dtype == BSATTN_BF16 && q->D == 64 && layout->block == 64 && layout->n_segments == 0 &&
+                 layout->window_tokens == 0 && head_mask == nullptr && q->N > 0 && q->N % 64 == 0 &&
+                 q->N / 64 <= 64 && k->stride_n <= (1 << 24) && v->stride_n <= (1 << 24);
+    Geometry g;
+    if (fused) fused = make_geometry(layout, q->N, budget, g) == BSATTN_OK && !g.is_dense && g.n_runs == 1 &&
+                       g.run_cls[0] == CLS_SPARSE && g.n_cand == q->N / 64;
+    if (!fused) {
+        bsattn_status st = bsattn_select(q, k, layout, budget, mask, workspace, workspace_bytes, stream);
+        if (st != BSATTN_OK) return st;
+        return bsattn_forward(q, k, v, mask, head_mask, scale, out, stream);
+    }
+    // the checks of bsattn_select and bsattn_forward
+    bsattn_status st;
+    if ((st = check_tensor(q)) != BSATTN_OK) return st;
+    if ((st = check_tensor(k)) != BSATTN_OK) return st;
+    if ((st = check_tensor(v)) != BSATTN_OK) return st;
+    if ((st = check_tensor(out)) != BSATTN_OK) return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype) return BSATTN_ERR_DTYPE;
+    if (k->B != q->B || v->B != q->B || out->B != q->B) return BSATTN_ERR_SHAPE;
+    if (k->N != q->N || v->N != q->N || out->N != q->N) return BSATTN_ERR_SHAPE;
+    if (k->D != q->D || v->D != q->D || out->D != q->D) return BSATTN_ERR_SHAPE;
+    if (v->H != k->H || out->H != q->H || q->H % k->H != 0) return BSATTN_ERR_SHAPE;
+    const int64_t nb = q->N / 64;
+    if (mask->B != q->B || mask->H != q->H || mask->nqb != nb || mask->nkb != nb) return BSATTN_ERR_SHAPE;
+    if (mask->mask == nullptr || mask->count == nullptr || mask->index == nullptr) return BSATTN_ERR_NULL;
+    if (!budget_ok(budget)) return BSATTN_ERR_BUDGET;
+    if (!(std::isfinite(scale))) return BSATTN_ERR_BUDGET;
+    if (q->B * (q->H + k->H) * g.n_cand > INT32_MAX) return BSATTN_ERR_SHAPE;
+    const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, 64, q->D);
+    if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;
+    if (workspace_bytes < need || ((uintptr_t)workspace) % 256 != 0) return BSATTN_ERR_WORKSPACE;
+
+    const hipStream_t s = (hipStream_t)stream;
+    mask->k = g.k;
+    mask->is_dense = 0;
+    float* qp = (float*)workspace;
+    float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
+    const int64_t pooled_bytes = q->B * (q->H + k->H) * g.n_cand * 64 * q->D * 2;
+    const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
+    hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g, qp, kp,
+                               xcd_groups, s);
+    if (e != hipSuccess) return BSATTN_ERR_HIP;
+    AttnArgs a{};
+    a.q = view_of(q);
+    a.k = view_of(k);
+    a.v = view_of(v);
+    a.o = out->data;
+    a.o_sb = out->stride_b;
+    a.o_sh = out->stride_h;
+    a.o_sn = out->stride_n;
+    a.B = (int32_t)q->B;
+    a.H = (int32_t)q->H;
+    a.Hkv = (int32_t)k->H;
+    a.nqb = (int32_t)nb;
+    a.nkb = (int32_t)nb;
+    a.mB = 1;
+    a.mH = 1;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    a.n_work = (int64_t)a.B * a.H * a.nqb;
+    a.qp = qp;
+    a.kp = kp;
+    a.prow = (int32_t)pooled_rows(g.n_cand);
+    a.keep = g.k;
+    a.m_out = mask->mask;
+    a.c_out = mask->count;
+    a.i_out = mask->index;
+    e = launch_attn_fused(a, s);
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
 

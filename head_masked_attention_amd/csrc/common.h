@@ -26,6 +26,16 @@ constexpr int kMaxCand = 2048;    // sparsifiable blocks handled by the selector
 // candidates, padded to whole 16-row tiles.
 __host__ __device__ __forceinline__ int64_t pooled_rows(int64_t n_cand) { return (n_cand + 15) / 16 * 16; }
 
+// Element (p, d) of a head's pooled sums in the selector workspace: 16-row
+// tiles stored in the order the score MFMA reads its operands (see the
+// selector source for the derivation).
+template <int D>
+__device__ __forceinline__ int64_t pooled_offset(int32_t p, int32_t d) {
+    constexpr int KQ = D / 4;
+    const int li = p & 15, gq = d / KQ, c = (d % KQ) >> 2, e = d & 3;
+    return (int64_t)(p >> 4) * 16 * D + ((c * 4 + gq) * 16 + li) * 4 + e;
+}
+
 // Per-layout geometry, host-computed once per call and passed by value.
 struct Geometry {
     int32_t nb;          // blocks in the sequence (N / block)

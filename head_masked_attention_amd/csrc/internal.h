@@ -19,6 +19,15 @@ struct AttnArgs {
     int64_t km_sb;               // batch stride of key_mask (0 = shared)
     float scale;                 // softmax scale (> 0)
     int64_t n_work;              // B * H * nqb workgroups of real work
+    // fused selection (bsattn_select_forward): the selector's pooled sums,
+    // the candidates kept per row, and the block mask written out
+    const float* qp;             // [B][H][prow][D], NULL in the plain forward
+    const float* kp;             // [B][Hkv][prow][D]
+    int32_t prow;                // pooled rows per head
+    int32_t keep;                // k
+    uint8_t* m_out;
+    int32_t* c_out;
+    int32_t* i_out;
 };
 
 // xcd_groups: the selector's two launches take their work in the attention
@@ -30,6 +39,10 @@ hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int
 hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
                              const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s);
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
+// bf16, D 64, block 64, every block a candidate (nkb <= 64), no head or key
+// mask: each workgroup ranks its own row from the pooled sums, writes the
+// row of the block mask and attends over the kept blocks.
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s);
 
 // bf16, block 64, D in {64, 128}: MFMA path.
 hipError_t launch_attn_mfma(const AttnArgs& a, int D, hipStream_t s);

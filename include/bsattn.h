@@ -226,6 +226,32 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
                              const uint8_t* head_mask, float scale,
                              bsattn_tensor* out, void* stream);
 
+/* Selection and attention in one call: the result of bsattn_select(q, k,
+ *  layout, budget, mask, ...) followed by bsattn_forward(q, k, v, mask,
+ *  head_mask, scale, out, ...).  The selection is the one the SD.Next commit
+ *  view of modules/attention/sparse computes (its selector paragraph:
+ *  mean-pooled block scores, diagonal first, top budget share of the
+ *  sparsifiable blocks) and the attention the block-sparse entry of the
+ *  inferensys glossary describes (softmax over the kept blocks only).
+ *  Arguments, layouts, ownership and errors are those of the two calls; mask
+ *  is an output here (mask, count and index written, k and is_dense set) and
+ *  is required.  workspace: bsattn_select_workspace_bytes(...) bytes,
+ *  256-byte aligned.
+ *  Where every block of the sequence is a candidate and a row fits one
+ *  wavefront -- bf16, D 64, block 64, no layout segments, no window, at most
+ *  64 blocks, a budget that keeps fewer than all of them, no head mask --
+ *  two kernels run: the block pooling, then one attention kernel whose
+ *  workgroups rank their own rows (the selector's keys and sort, so the
+ *  same masks up to near-ties within 2^-14 relative, where the two fp32
+ *  summation orders may differ) and attend over the kept blocks; otherwise
+ *  the two calls run as written.  Enqueues only; never synchronises.
+ */
+bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor* k,
+                                    const bsattn_tensor* v, const bsattn_layout* layout,
+                                    double budget, const uint8_t* head_mask, float scale,
+                                    bsattn_tensor* out, bsattn_block_mask* mask,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * bsattn_forward with a per-token key mask composed with the block mask
  * (SD.Next sparse-stage paragraph: a backend declaring masked_block takes the

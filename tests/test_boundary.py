@@ -175,6 +175,20 @@ def test_select_item_count_limit(lib):
     assert call_select(lib, q, k, lay, 0.3, bmask(B=B, H=H, nb=64)) == 7
 
 
+def test_select_forward_validation(lib):
+    # the fused shape (bf16, D 64, block 64, no segments, <= 64 blocks) and one that runs the two calls
+    lay, _k = layout()
+    for N, D in ((64 * 16, 64), (64 * 16, 128)):
+        q, k, v, out = tensor(N=N, D=D), tensor(N=N, D=D), tensor(N=N, D=D), tensor(N=N, D=D)
+        call = lambda m, budget=0.3, ws=FAKE: lib.bsattn_select_forward(
+            ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(lay), budget, None, 0.0,
+            ctypes.byref(out), None if m is None else ctypes.byref(m), ws, 1 << 30, None)
+        assert call(None) == 1                          # the mask is an output here: required
+        assert call(bmask(nb=8)) == 3                   # wrong number of blocks
+        assert call(bmask(nb=16), budget=0.0) == 6      # budget out of range
+        assert call(bmask(nb=16), ws=None) == 7         # no workspace
+
+
 def call_forward(lib, q, k, v, m, out, scale=0.0):
     return lib.bsattn_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                               None if m is None else ctypes.byref(m), None, scale,

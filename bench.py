@@ -1,9 +1,12 @@
 """Benchmark of the block-sparse, head-masked attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: bsattn_select (block
-sums, scores, rank, pins, compaction) followed by bsattn_forward (attention
-over the kept blocks, head-masked) on synthetic inputs already resident in
-HBM.  The default workload is the SDXL self-attention shape (B=2 CFG pair,
+A step is one pass of the whole path over one batch: block sums, scores,
+rank, pins, compaction and attention over the kept blocks (head-masked), on
+synthetic inputs already resident in HBM.  It runs as bsattn_select_forward,
+which ranks inside the attention kernel where that kernel applies (bf16, D 64,
+block 64, every block a candidate, at most 64 blocks, no head mask) and is
+bsattn_select followed by bsattn_forward elsewhere; `two_call_ms_per_step`
+times the same step as the two calls (--two-calls makes them the step).  The default workload is the SDXL self-attention shape (B=2 CFG pair,
 10 heads, 64x64 latent = 4096 tokens, head_dim 64, 64-token blocks, 30%
 budget) — the shape the SD.Next commit page quotes its timings on.
 

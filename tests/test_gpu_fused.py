@@ -101,3 +101,22 @@ def test_fused_with_head_mask_runs_the_two_calls(cuda):
     torch.cuda.synchronize()
     assert torch.equal(out, out_sep)
     assert bool(torch.all(out[:, 1] == 0))
+
+
+def test_fused_strided_views(cuda):
+    # [B, N, H, D] storage viewed as [B, H, N, D] for Q, K, V and the output
+    B, H, nb, D = 2, 4, 24, 64
+    N = 64 * nb
+    g = torch.Generator().manual_seed(304)
+    base = [torch.randn((B, N, H, D), generator=g).to(torch.bfloat16) for _ in range(3)]
+    q, k, v = (t.to(cuda).transpose(1, 2) for t in base)
+    out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=cuda).transpose(1, 2)
+    got_out, bm = hm.select_forward(q, k, v, hm.Layout(64, []), 0.3, out=out)
+    torch.cuda.synchronize()
+    assert got_out.data_ptr() == out.data_ptr()
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    mask, tie = oracle.select(q64, k64, 64, [], 0.3)
+    compare_masks(bm, mask, tie)
+    keep_rows = np.repeat(tie == 0, 64, axis=-1)
+    ref = oracle.attention(q64, k64, v64, 64, mask)
+    assert_close(to64(out)[keep_rows], ref[keep_rows], "bf16", "fused strided views")

@@ -53,6 +53,7 @@ CASES = [
     ("max_64_blocks_gqa", 1, 4, 2, 64, 0.25),
     ("mqa_low_budget", 1, 4, 1, 20, 0.05),
     ("two_blocks", 1, 2, 2, 2, 0.5),
+    ("all_but_one_block", 1, 2, 2, 20, 0.95),     # k = n - 1: near-full lists, still selective
 ]
 
 

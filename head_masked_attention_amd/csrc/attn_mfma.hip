@@ -290,7 +290,7 @@ void attn_mfma_kernel(AttnArgs a) {
     __shared__ uint8_t s_flag[FUSED ? 64 : 1];
     if constexpr (FUSED) {
         if (wave == 0) fused_rank_row(a, b, h, kvh, qb, lane, s_list, s_flag);
-        __syncthreads();
+        lds_barrier();                       // the list in LDS; the mask row's stores drain meanwhile
         cnt = a.keep;
         blk0 = s_list[grp];                  // unused when the group has no block
     }

@@ -144,11 +144,45 @@ enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 // writes the row's mask, count and ascending index list, and leaves the list
 // in LDS for the stage loop.
 __device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, int kvh, int qb, int lane,
-                                               int32_t* s_list, uint8_t* s_flag) {
+                                               int32_t* s_list, uint8_t* s_flag, float* s_qsum) {
     constexpr uint32_t IMASK = 63u;           // 64 candidate positions
     const int n = a.nkb;
-    const float* qrow = a.qp + ((int64_t)b * a.H + h) * a.prow * 64;
     const float* krow = a.kp + ((int64_t)b * a.Hkv + kvh) * a.prow * 64;
+    // the query block's sum over its 64 tokens, added in the selector's
+    // pooling order (token rows lane / 8 + 8 l of chunk lane % 8, then across
+    // the lanes of one chunk), so that it equals the pooled query sum bit for
+    // bit; lanes 0..7 store dimensions 8 lane .. 8 lane + 7 to LDS while the
+    // whole wavefront is active, and every lane reads the sum back from there
+    {
+        float qs[8];
+        const uint16_t* qsrc = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh +
+                               ((int64_t)qb * 64 + lane / 8) * a.q.sn + (lane % 8) * 8;
+        uint4 raw[8];
+#pragma unroll
+        for (int l = 0; l < 8; ++l) raw[l] = *(const uint4*)(qsrc + (int64_t)l * 8 * a.q.sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[e] = 0.f;
+#pragma unroll
+        for (int l = 0; l < 8; ++l) {
+            const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qs[2 * e] += __uint_as_float(w[e] << 16);
+                qs[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qs[e] += __uint_as_float(lane_xor(__float_as_uint(qs[e]), off));
+        if (lane < 8) {
+            *(float4*)(s_qsum + 8 * lane) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+            *(float4*)(s_qsum + 8 * lane + 4) = make_float4(qs[4], qs[5], qs[6], qs[7]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     uint32_t key[1][1] = {{0u}};
     if (lane < n) {
         if (lane == qb) {
@@ -157,7 +191,7 @@ __device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, 
             float sc = 0.f;
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
-                const float4 q4 = *(const float4*)(qrow + pooled_offset<64>(qb, 4 * m));
+                const float4 q4 = *(const float4*)(s_qsum + 4 * m);
                 const float4 k4 = *(const float4*)(krow + pooled_offset<64>(lane, 4 * m));
                 sc = fmaf(q4.x, k4.x, sc);
                 sc = fmaf(q4.y, k4.y, sc);
@@ -288,8 +322,9 @@ void attn_mfma_kernel(AttnArgs a) {
     }
     __shared__ int32_t s_list[FUSED ? 64 : 1];
     __shared__ uint8_t s_flag[FUSED ? 64 : 1];
+    __shared__ __attribute__((aligned(16))) float s_qsum[FUSED ? 64 : 4];
     if constexpr (FUSED) {
-        if (wave == 0) fused_rank_row(a, b, h, kvh, qb, lane, s_list, s_flag);
+        if (wave == 0) fused_rank_row(a, b, h, kvh, qb, lane, s_list, s_flag, s_qsum);
         lds_barrier();                       // the list in LDS; the mask row's stores drain meanwhile
         cnt = a.keep;
         blk0 = s_list[grp];                  // unused when the group has no block

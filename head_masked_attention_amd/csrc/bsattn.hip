@@ -458,12 +458,12 @@ bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor*
     const hipStream_t s = (hipStream_t)stream;
     mask->k = g.k;
     mask->is_dense = 0;
-    float* qp = (float*)workspace;
+    // K's block sums only: each attention workgroup sums its own query block
     float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
-    const int64_t pooled_bytes = q->B * (q->H + k->H) * g.n_cand * 64 * q->D * 2;
+    const int64_t pooled_bytes = q->B * k->H * g.n_cand * 64 * q->D * 2;
     const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
-    hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g, qp, kp,
-                               xcd_groups, s);
+    hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g, nullptr,
+                               kp, xcd_groups, s);
     if (e != hipSuccess) return BSATTN_ERR_HIP;
     AttnArgs a{};
     a.q = view_of(q);
@@ -482,7 +482,6 @@ bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor*
     a.mH = 1;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     a.n_work = (int64_t)a.B * a.H * a.nqb;
-    a.qp = qp;
     a.kp = kp;
     a.prow = (int32_t)pooled_rows(g.n_cand);
     a.keep = g.k;

@@ -19,10 +19,10 @@ struct AttnArgs {
     int64_t km_sb;               // batch stride of key_mask (0 = shared)
     float scale;                 // softmax scale (> 0)
     int64_t n_work;              // B * H * nqb workgroups of real work
-    // fused selection (bsattn_select_forward): the selector's pooled sums,
-    // the candidates kept per row, and the block mask written out
-    const float* qp;             // [B][H][prow][D], NULL in the plain forward
-    const float* kp;             // [B][Hkv][prow][D]
+    // fused selection (bsattn_select_forward): the selector's pooled key
+    // sums (each workgroup sums its own query block), the candidates kept
+    // per row, and the block mask written out
+    const float* kp;             // [B][Hkv][prow][D], NULL in the plain forward
     int32_t prow;                // pooled rows per head
     int32_t keep;                // k
     uint8_t* m_out;
@@ -34,14 +34,16 @@ struct AttnArgs {
 // kernel's XCD-grouped (b, K/V head) order, so that pooled sums, masks and
 // lists are written by the XCD whose attention workgroups read them next
 // (chosen by the host when an XCD's share of Q and K fits in its L2).
+// qp NULL: pool K only.
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
                        int Hkv, const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s);
 hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
                              const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s);
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
 // bf16, D 64, block 64, every block a candidate (nkb <= 64), no head or key
-// mask: each workgroup ranks its own row from the pooled sums, writes the
-// row of the block mask and attends over the kept blocks.
+// mask: each workgroup sums its query block, ranks its row against the
+// pooled key sums, writes the row of the block mask and attends over the
+// kept blocks.
 hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s);
 
 // bf16, block 64, D in {64, 128}: MFMA path.

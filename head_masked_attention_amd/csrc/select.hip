@@ -44,7 +44,7 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // kernel, so that the XCD that pools a group's Q and K is the one whose
 // attention workgroups read them next, from its L2 when an XCD's share fits
 // there (the host decides).  Otherwise the plain order (tensor, b, head,
-// block).
+// block).  qp NULL: K only (the fused attention sums its own query block).
 template <typename T, int D, int BLOCK>
 __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int H, int Hkv,
                                                    Geometry g, float* __restrict__ qp,
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     // 32-bit index arithmetic (the host checks that the items fit): the
     // division sequences sit in front of every wavefront's loads
     const uint32_t nc = (uint32_t)g.n_cand;
-    const uint32_t nq = (uint32_t)B * (uint32_t)H * nc, nk = (uint32_t)B * (uint32_t)Hkv * nc;
+    const uint32_t nq = qp == nullptr ? 0u : (uint32_t)B * (uint32_t)H * nc, nk = (uint32_t)B * (uint32_t)Hkv * nc;
     // which tensor, (b, head) and candidate this wavefront pools; the
     // tensor's fields are selected by value (a pointer to a kernel argument
     // would put both views in scratch memory)
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     if (xcd_groups) {
         const uint32_t item = (uint32_t)xcd_logical_id(blockIdx.x, gridDim.x) * 4u + wave;   // grid: a multiple of 8
         if (item >= nq + nk) return;
-        const uint32_t rep = (uint32_t)(H / Hkv);
+        const uint32_t rep = qp == nullptr ? 0u : (uint32_t)(H / Hkv);
         const uint32_t per_group = (rep + 1) * nc;
         const uint32_t grp = item / per_group, r = item - grp * per_group;
         b = grp / (uint32_t)Hkv;
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
 template <typename T, int D>
 static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
                                 const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s) {
-    const int64_t items = (int64_t)B * (H + Hkv) * g.n_cand;
+    const int64_t items = (int64_t)B * ((qp == nullptr ? 0 : H) + Hkv) * g.n_cand;
     const int64_t wgs = (items + 3) / 4;
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
     if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);

@@ -240,8 +240,9 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
  *  Where every block of the sequence is a candidate and a row fits one
  *  wavefront -- bf16, D 64, block 64, no layout segments, no window, at most
  *  64 blocks, a budget that keeps fewer than all of them, no head mask --
- *  two kernels run: the block pooling, then one attention kernel whose
- *  workgroups rank their own rows (the selector's keys and sort, so the
+ *  two kernels run: the block pooling of K, then one attention kernel whose
+ *  workgroups sum their own query block and rank their own rows (the query
+ *  sums equal the pooled ones bit for bit; the selector's keys and sort, so the
  *  same masks up to near-ties within 2^-14 relative, where the two fp32
  *  summation orders may differ) and attend over the kept blocks; otherwise
  *  the two calls run as written.  Enqueues only; never synchronises.

@@ -137,8 +137,9 @@ enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 // K/V stage tile is loaded into LDS once (by all four wavefronts) and read
 // by both heads; there is no merge, each pair writes its own head.
 // FUSED (bsattn_select_forward; D 64, every block of the sequence a candidate,
-// at most 64 of them): wavefront 0 ranks the workgroup's row from the
-// selector's pooled sums -- the same 32-bit keys and wavefront bitonic sort
+// at most 64 of them): wavefront 0 ranks the workgroup's row from its own
+// query block's sum and the selector's pooled key sums -- the same 32-bit
+// keys and wavefront bitonic sort
 // as the selector's ranking: the diagonal first, then by score with ties to
 // the lower block, truncated to 2^-14 relative -- keeps the top `keep`,
 // writes the row's mask, count and ascending index list, and leaves the list

@@ -139,11 +139,10 @@ enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 // FUSED (bsattn_select_forward; D 64, every block of the sequence a candidate,
 // at most 64 of them): wavefront 0 ranks the workgroup's row from its own
 // query block's sum and the selector's pooled key sums -- the same 32-bit
-// keys and wavefront bitonic sort
-// as the selector's ranking: the diagonal first, then by score with ties to
-// the lower block, truncated to 2^-14 relative -- keeps the top `keep`,
-// writes the row's mask, count and ascending index list, and leaves the list
-// in LDS for the stage loop.
+// keys and wavefront bitonic sort as the selector's ranking: the diagonal
+// first, then by score with ties to the lower block, truncated to 2^-14
+// relative -- keeps the top `keep`, writes the row's mask, count and
+// ascending index list, and leaves the list in LDS for the stage loop.
 __device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, int kvh, int qb, int lane,
                                                int32_t* s_list, uint8_t* s_flag, float* s_qsum) {
     constexpr uint32_t IMASK = 63u;           // 64 candidate positions

@@ -64,6 +64,18 @@ def test_fused_small(cuda, case):
     check_fused(cuda, q, k, v, [], 64, budget, what=name)
 
 
+def test_fused_mixed_magnitude_queries(cuda):
+    # query elements spread over seven binades (each scaled by 2^e, e in
+    # -6..0, seeded): the 64-token block sums round in fp32, so their value
+    # depends on the order of the additions, which the workgroup's own query
+    # sum keeps equal to the pool kernel's
+    q, k, v = workloads.small_case(B=1, H=4, Hkv=2, N=64 * 48, D=64, seed=303)
+    g = torch.Generator().manual_seed(304)
+    e = torch.randint(-6, 1, q.shape, generator=g).float()
+    q = (q.float() * torch.exp2(e)).to(q.dtype)
+    check_fused(cuda, q, k, v, [], 64, 0.3, what="mixed-magnitude queries")
+
+
 FALLBACK = [
     # shapes the fused kernel does not take: the two calls run
     ("layout_segments", 1, 2, 2, 64 * 12, 64, 64, (("text", 64), ("image", 64 * 11)), 0.3, 0),

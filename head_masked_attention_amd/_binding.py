@@ -209,6 +209,20 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for allocating a call's temporaries and outputs.
+
+    The caching allocator hands a freed block back out only to work on the
+    stream it was allocated on.  Buffers that the library's kernels read or
+    write on `stream` are therefore allocated on `stream` itself: a temporary
+    (workspace, an internal block mask) dropped on return cannot be reused by
+    other work until the kernels queued before it on that stream are done.
+    """
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def empty_block_mask(B: int, H: int, nb: int, device) -> BlockMask:
     import torch
     return BlockMask(torch.empty((B, H, nb, nb), dtype=torch.uint8, device=device),
@@ -227,11 +241,12 @@ def select(q, k, layout: Layout, budget: float, *, out: BlockMask | None = None,
     lib = load_library()
     B, H, N, D = q.shape
     nb = N // layout.block
-    if out is None:
-        out = empty_block_mask(B, H, nb, q.device)
     need = select_workspace_bytes(B, H, k.shape[1], N, layout.block, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = empty_block_mask(B, H, nb, q.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     tq, tk = _tensor(q), _tensor(k)
     lay, _keep = layout._c()
     bm = out._c()
@@ -251,13 +266,14 @@ def select_forward(q, k, v, layout: Layout, budget: float, head_mask=None, scale
     lib = load_library()
     B, H, N, D = q.shape
     nb = N // layout.block
-    if block_mask is None:
-        block_mask = empty_block_mask(B, H, nb, q.device)
-    if out is None:
-        out = torch.empty_like(q)
     need = select_workspace_bytes(B, H, k.shape[1], N, layout.block, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if block_mask is None:
+            block_mask = empty_block_mask(B, H, nb, q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     hm_ptr = None
     if head_mask is not None:
         if head_mask.dtype != torch.uint8 or not head_mask.is_cuda or head_mask.numel() != H:
@@ -281,7 +297,8 @@ def radial(layout: Layout, N: int, density: float, *, B: int = 1, H: int = 1, de
     lib = load_library()
     nb = N // layout.block
     if out is None:
-        out = empty_block_mask(B, H, nb, device if device is not None else torch.device("cuda"))
+        with _on(stream):
+            out = empty_block_mask(B, H, nb, device if device is not None else torch.device("cuda"))
     lay, _keep = layout._c()
     bm = out._c()
     st = lib.bsattn_radial(ctypes.byref(lay), float(density), ctypes.byref(bm),
@@ -301,7 +318,8 @@ def forward(q, k, v, block_mask: BlockMask | None = None, head_mask=None, scale:
     import torch
     lib = load_library()
     if out is None:
-        out = torch.empty_like(q)
+        with _on(stream):
+            out = torch.empty_like(q)
     tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     bm = None if block_mask is None else block_mask._c()
     hm = None
@@ -330,12 +348,13 @@ def quantize_fp8(x, *, out=None, scale=None, workspace=None, stream=None):
     import torch
     lib = load_library()
     B, H = x.shape[0], x.shape[1]
-    if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if scale is None:
-        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
-    if workspace is None:
-        workspace = torch.empty(B * H, dtype=torch.int32, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if scale is None:
+            scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(B * H, dtype=torch.int32, device=x.device)
     tx, to = _tensor(x), _tensor(out)
     st = lib.bsattn_quantize_fp8(ctypes.byref(tx), ctypes.byref(to), scale.data_ptr(), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream(x.device, stream))
@@ -367,7 +386,8 @@ def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_mask: BlockMask | N
     lib = load_library()
     where = "bsattn_forward_fp8" if key_mask is None else "bsattn_forward_fp8_masked"
     if out is None:
-        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+        with _on(stream):
+            out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     for name, sc, heads in (("q_scale", q_scale, q8.shape[1]), ("k_scale", k_scale, k8.shape[1]),
                             ("v_scale", v_scale, v8.shape[1])):
         if sc.dtype != torch.float32 or not sc.is_cuda or not sc.is_contiguous() or sc.numel() != q8.shape[0] * heads:

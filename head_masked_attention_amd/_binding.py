@@ -62,7 +62,7 @@ EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8", "bsattn_forward_fp8_masked",
            "bsattn_head_mask", "bsattn_mask_density", "bsattn_select_forward",
            "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
-           "bsattn_stage_outcome_string"]
+           "bsattn_stage_outcome_string", "bsattn_select_no_alloc"]
 
 class _StageConfig(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("min_length", ctypes.c_int64), ("n_steps", ctypes.c_int32),
@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH):
                                   ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P,
                                   ctypes.c_size_t, P]
     lib.bsattn_radial.argtypes = [ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
+    lib.bsattn_select_no_alloc.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                           ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
     lib.bsattn_select_forward.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                           ctypes.POINTER(_Layout), dbl, P, ctypes.c_float, ctypes.POINTER(_Tensor),
                                           ctypes.POINTER(_BlockMask), P, ctypes.c_size_t, P]
@@ -254,6 +256,21 @@ def select(q, k, layout: Layout, budget: float, *, out: BlockMask | None = None,
                            ctypes.byref(bm), workspace.data_ptr(), workspace.numel(),
                            _stream(q.device, stream))
     _check(st, "bsattn_select")
+    out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
+    return out
+
+
+def select_no_alloc(q, k, layout: Layout, budget: float, *, out: BlockMask, stream=None) -> BlockMask:
+    """bsattn_select_no_alloc: bsattn_select with the library's static
+    per-GPU scratch in place of a workspace; `out` is required, so the call
+    allocates nothing.  Calls overlapping on one GPU share the scratch."""
+    lib = load_library()
+    tq, tk = _tensor(q), _tensor(k)
+    lay, _keep = layout._c()
+    bm = out._c()
+    st = lib.bsattn_select_no_alloc(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(lay), float(budget),
+                                    ctypes.byref(bm), _stream(q.device, stream))
+    _check(st, "bsattn_select_no_alloc")
     out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
     return out
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/bsattn.h"
@@ -48,12 +49,16 @@ bool budget_ok(double x) { return std::isfinite(x) && x > 0.0; }
 
 // Block classes from ordered segments: a block is DROPPED when every segment
 // it overlaps is padding, SPARSE when it lies inside one image/video segment,
-// PINNED otherwise.  Returns false on a malformed layout.
-bool compute_classes(const bsattn_layout* lay, int64_t N, std::vector<int32_t>& cls) {
+// PINNED otherwise.  Calls f(block, class) for every block in order (no heap
+// allocation).  Returns false on a malformed layout, before any call of f.
+template <typename F>
+bool for_each_block_class(const bsattn_layout* lay, int64_t N, F f) {
     const int64_t block = lay->block;
     const int64_t nb = N / block;
-    cls.assign((size_t)nb, CLS_SPARSE);
-    if (lay->n_segments == 0) return true;
+    if (lay->n_segments == 0) {
+        for (int64_t b = 0; b < nb; ++b) f(b, (int32_t)CLS_SPARSE);
+        return true;
+    }
     int64_t total = 0;
     for (int s = 0; s < lay->n_segments; ++s) {
         const bsattn_segment& sg = lay->segments[s];
@@ -74,7 +79,7 @@ bool compute_classes(const bsattn_layout* lay, int64_t N, std::vector<int32_t>& 
             if (kd != BSATTN_SEG_IMAGE && kd != BSATTN_SEG_VIDEO) sparsifiable = false;
             if (u != s) single = false;
         }
-        cls[(size_t)b] = all_pad ? CLS_DROPPED : (single && sparsifiable) ? CLS_SPARSE : CLS_PINNED;
+        f(b, (int32_t)(all_pad ? CLS_DROPPED : (single && sparsifiable) ? CLS_SPARSE : CLS_PINNED));
     }
     return true;
 }
@@ -106,24 +111,25 @@ bsattn_status check_layout(const bsattn_layout* lay) {
 }
 
 bsattn_status make_geometry(const bsattn_layout* lay, int64_t N, double budget, Geometry& g) {
-    std::vector<int32_t> cls;
-    if (!compute_classes(lay, N, cls)) return BSATTN_ERR_LAYOUT;
     std::memset(&g, 0, sizeof g);
     g.nb = (int32_t)(N / lay->block);
     g.block = lay->block;
+    // run-length classes, built while the classes are computed
     int32_t n_sparse = 0, n_other = 0, runs = 0;
-    for (int32_t b = 0; b < g.nb;) {
-        int32_t e = b;
-        while (e < g.nb && cls[(size_t)e] == cls[(size_t)b]) ++e;
-        if (runs == kMaxRuns) return BSATTN_ERR_LAYOUT;
-        g.run_first[runs] = b;
-        g.run_len[runs] = e - b;
-        g.run_cls[runs] = cls[(size_t)b];
-        if (cls[(size_t)b] == CLS_SPARSE) { g.run_off[runs] = n_sparse; n_sparse += e - b; }
-        else { g.run_off[runs] = n_other; n_other += e - b; }
-        ++runs;
-        b = e;
-    }
+    bool too_many = false;
+    const bool ok = for_each_block_class(lay, N, [&](int64_t b, int32_t cls) {
+        if (runs > 0 && g.run_cls[runs - 1] == cls) { ++g.run_len[runs - 1]; }
+        else if (runs == kMaxRuns) { too_many = true; return; }
+        else {
+            g.run_first[runs] = (int32_t)b;
+            g.run_len[runs] = 1;
+            g.run_cls[runs] = cls;
+            g.run_off[runs] = cls == CLS_SPARSE ? n_sparse : n_other;
+            ++runs;
+        }
+        if (cls == CLS_SPARSE) ++n_sparse; else ++n_other;
+    });
+    if (!ok || too_many) return BSATTN_ERR_LAYOUT;
     g.n_runs = runs;
     g.n_cand = n_sparse;
     g.n_other = n_other;
@@ -167,13 +173,12 @@ bsattn_status bsattn_layout_classes(const bsattn_layout* layout, int64_t N, uint
     if (st != BSATTN_OK) return st;
     if (classes == nullptr || n_cand == nullptr) return BSATTN_ERR_NULL;
     if (N <= 0 || N % layout->block != 0 || N / layout->block > INT32_MAX) return BSATTN_ERR_SHAPE;
-    std::vector<int32_t> cls;
-    if (!compute_classes(layout, N, cls)) return BSATTN_ERR_LAYOUT;
     int32_t nc = 0;
-    for (size_t b = 0; b < cls.size(); ++b) {
-        classes[b] = (uint8_t)cls[b];
-        nc += cls[b] == CLS_SPARSE;
-    }
+    if (!for_each_block_class(layout, N, [&](int64_t b, int32_t cls) {
+            classes[b] = (uint8_t)cls;
+            nc += cls == CLS_SPARSE;
+        }))
+        return BSATTN_ERR_LAYOUT;
     *n_cand = nc;
     return BSATTN_OK;
 }
@@ -193,9 +198,12 @@ size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t 
     return align256((size_t)B * H * rows * D * 4) + align256((size_t)B * Hkv * rows * D * 4);
 }
 
-bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
-                            const bsattn_layout* layout, double budget, bsattn_block_mask* out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Validation and geometry of a selection call (no HIP call).
+bsattn_status select_validate(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_layout* layout,
+                              double budget, const bsattn_block_mask* out, Geometry& g) {
     bsattn_status st;
     if ((st = check_tensor(q)) != BSATTN_OK) return st;
     if ((st = check_tensor(k)) != BSATTN_OK) return st;
@@ -209,18 +217,16 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
     const int64_t nb = q->N / layout->block;
     if (out->B != q->B || out->H != q->H || out->nqb != nb) return BSATTN_ERR_SHAPE;
     if (!budget_ok(budget)) return BSATTN_ERR_BUDGET;
-    Geometry g;
     if ((st = make_geometry(layout, q->N, budget, g)) != BSATTN_OK) return st;
     if (!g.is_dense && g.n_cand > kMaxCand) return BSATTN_ERR_UNSUPPORTED;
     // the pool kernel indexes its (tensor, b, head, candidate) items in 32 bits
     if (!g.is_dense && q->B * (q->H + k->H) * g.n_cand > INT32_MAX) return BSATTN_ERR_SHAPE;
-    const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, layout->block, q->D);
-    if (!g.is_dense) {
-        if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;
-        if (workspace_bytes < need || ((uintptr_t)workspace) % 256 != 0) return BSATTN_ERR_WORKSPACE;
-    }
+    return BSATTN_OK;
+}
 
-    const hipStream_t s = (hipStream_t)stream;
+// The launches of a validated selection; `workspace` holds the pooled sums.
+bsattn_status select_launch(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_layout* layout,
+                            const Geometry& g, bsattn_block_mask* out, void* workspace, hipStream_t s) {
     const MaskOut mo{out->mask, out->count, out->index};
     out->k = g.k;
     out->is_dense = g.is_dense;
@@ -241,6 +247,76 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
             e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, xcd_groups, s);
     }
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
+                            const bsattn_layout* layout, double budget, bsattn_block_mask* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    Geometry g;
+    const bsattn_status st = select_validate(q, k, layout, budget, out, g);
+    if (st != BSATTN_OK) return st;
+    if (!g.is_dense) {
+        const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, layout->block, q->D);
+        if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;
+        if (workspace_bytes < need || ((uintptr_t)workspace) % 256 != 0) return BSATTN_ERR_WORKSPACE;
+    }
+    return select_launch(q, k, layout, g, out, workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Selection without a caller workspace, for callers that cannot allocate
+// device memory.  The pooled sums live in `scratch`, a file-scope device
+// array that the code object carries: each GPU the library runs on holds its
+// own copy, at its own address, until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.  Every call on one GPU shares the
+// array, so calls that overlap on one GPU race.  Nothing in it has to start
+// at zero: the pool kernel writes every sum the score kernel reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[BSATTN_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on its first use).
+bsattn_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return BSATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return BSATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BSATTN_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BSATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bsattn_status bsattn_select_no_alloc(const bsattn_tensor* q, const bsattn_tensor* k,
+                                     const bsattn_layout* layout, double budget,
+                                     bsattn_block_mask* out, void* stream) {
+    Geometry g;
+    bsattn_status st = select_validate(q, k, layout, budget, out, g);
+    if (st != BSATTN_OK) return st;
+    void* ws = nullptr;
+    if (!g.is_dense) {
+        const size_t need = bsattn_select_workspace_bytes(q->B, q->H, k->H, q->N, layout->block, q->D);
+        if (need > (size_t)BSATTN_NO_ALLOC_SCRATCH_BYTES) return BSATTN_ERR_WORKSPACE;
+        if ((st = scratch_address(&ws)) != BSATTN_OK) return st;
+    }
+    return select_launch(q, k, layout, g, out, ws, (hipStream_t)stream);
 }
 
 bsattn_status bsattn_quantize_fp8(const bsattn_tensor* x, bsattn_tensor* out, float* scale, void* ws,

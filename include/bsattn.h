@@ -3,8 +3,10 @@
  * AMD Instinct MI355X (gfx950).
  *
  * C ABI.  Plain pointers and sizes only.  Device buffers are allocated by the
- * caller; the library allocates no device memory, keeps no device state and
- * keeps no pointer after a call returns.  Every GPU call only enqueues work on
+ * caller; the library allocates no device memory and keeps no pointer to a
+ * caller's buffer after a call returns.  The device state it holds is fixed
+ * at load: the kernels' code objects and, per GPU, the static scratch array
+ * of bsattn_select_no_alloc.  Every GPU call only enqueues work on
  * the caller's HIP stream (passed as `void*`, a hipStream_t; NULL = the null
  * stream) and never synchronises, except bsattn_mask_density, which is meant
  * to be called off the hot path.
@@ -14,9 +16,12 @@
  * launch returns BSATTN_ERR_HIP.  Device faults surface at the caller's next
  * synchronisation.  Nothing is printed and nothing exits.
  *
- * The library is stateless, so calls are thread-safe.  Calls that share
- * output buffers on one stream are ordered by the stream; across streams the
- * caller orders them.
+ * Host state: a per-device table of the scratch array's address (filled on
+ * first use, under a lock) and a per-device occupancy figure of the fp8
+ * kernel; the stage objects are the caller's.  Calls are thread-safe except
+ * that bsattn_select_no_alloc calls overlapping on one GPU share its
+ * scratch.  Calls that share output buffers on one stream are ordered by the
+ * stream; across streams the caller orders them.
  *
  * Sources, pages in the reference bundle:
  *  - SD.Next commit view, modules/attention/sparse: the selector paragraph,
@@ -190,6 +195,25 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
                             const bsattn_layout* layout, double budget,
                             bsattn_block_mask* out, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * bsattn_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results, validation and errors as bsattn_select, without
+ * the workspace: the pooled sums go to a static device array of
+ * BSATTN_NO_ALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends.  The call allocates nothing (no hipMalloc, no hipFree);
+ * its first use on a device looks up that device's address of the array.
+ *  BSATTN_ERR_WORKSPACE when bsattn_select_workspace_bytes(...) for these
+ *  sizes exceeds BSATTN_NO_ALLOC_SCRATCH_BYTES.
+ * All calls on one GPU share the array and it keeps the last call's
+ * contents: calls that overlap on one GPU (several streams, several host
+ * threads) race and must be ordered by the caller.
+ */
+#define BSATTN_NO_ALLOC_SCRATCH_BYTES (16u << 20)
+bsattn_status bsattn_select_no_alloc(const bsattn_tensor* q, const bsattn_tensor* k,
+                                     const bsattn_layout* layout, double budget,
+                                     bsattn_block_mask* out, void* stream);
 
 /*
  * Radial control (SD.Next radial-control paragraph): every SPARSE row keeps

@@ -142,6 +142,28 @@ def test_select_validation(lib):
         assert out.k == -7 and out.is_dense == -7          # untouched on error
 
 
+def test_select_no_alloc_validation(lib):
+    """bsattn_select_no_alloc: the validation codes of bsattn_select, and
+    BSATTN_ERR_WORKSPACE when the pooled sums would not fit its scratch --
+    all returned before any HIP call (so on the CPU too)."""
+    lay, _k = layout()
+    for over, code in [(dict(q=tensor(data=0)), 1), (dict(q=tensor(D=48)), 3), (dict(budget=0.0), 6),
+                       (dict(out=bmask(nb=5)), 3)]:
+        args = dict(q=tensor(), k=tensor(), budget=0.3, out=bmask())
+        args.update(over)
+        st = lib.bsattn_select_no_alloc(ctypes.byref(args["q"]), ctypes.byref(args["k"]), ctypes.byref(lay),
+                                        args["budget"], ctypes.byref(args["out"]), None)
+        assert st == code, (over, st)
+        assert args["out"].k == -7
+    # 64 heads x 1024 blocks x D 128: 64 MiB of pooled sums, over the 16 MiB scratch
+    big = tensor(H=64, N=64 * 1024, D=128)
+    out = bmask(H=64, nb=1024)
+    assert B_.select_workspace_bytes(1, 64, 64, 64 * 1024, 64, 128) > 16 << 20
+    st = lib.bsattn_select_no_alloc(ctypes.byref(big), ctypes.byref(big), ctypes.byref(lay), 0.3,
+                                    ctypes.byref(out), None)
+    assert st == 7 and out.k == -7
+
+
 def test_select_layout_errors(lib):
     q, k = tensor(), tensor()
     for segs, code in [([("text", 100)], 5), ([("image", 128), ("text", 100)], 5),

@@ -15,7 +15,11 @@ step (kept FLOPs / step time).  `roofline` covers the attention kernel (MFMA
 bound); `selector` reports the selector's algorithmic GB/s against HBM;
 `speedup_vs_dense` compares the same attention kernel at full density (budget
 1.0, same layout and head mask).  `cpu_baseline` times the fp64 CPU oracle on
-the same workload on this host's cores.
+the same workload on this host's cores.  `per_config` repeats the step,
+roofline, selector and speedup figures for every configuration (tiny fp32,
+SDXL, joint text+image, video with its radial control, the 64-layer
+head-masked stack with its head-mask skip); `reference` gives the platform's
+own bf16 GEMM and dense sdpa rates on this GPU as context.
 """
 from __future__ import annotations
 
@@ -37,6 +41,10 @@ import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+FP32_PEAK_TFLOPS = 157.3           # MI355X fp32 vector (the fp32 path runs on the VALU)
+# the configurations reported under per_config: tiny fp32, SDXL, joint
+# text+image, video (with the radial control), the 64-layer head-masked stack
+PER_CONFIG = ["tiny_fp32", "sdxl_bf16", "joint_text_image_bf16", "video_radial_bf16", "head_masked_stack_bf16"]
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 ATTN_SOURCES = ["head_masked_attention_amd/csrc/attn_mfma.hip", "head_masked_attention_amd/csrc/common.h",
                 "head_masked_attention_amd/csrc/rank.h",
@@ -86,6 +94,10 @@ def parse():
     p.add_argument("--two-calls", action="store_true",
                    help="run the step as bsattn_select + bsattn_forward even where bsattn_select_forward "
                         "fuses the ranking into the attention kernel")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip the per-configuration figures of every workload")
+    p.add_argument("--no-reference", action="store_true",
+                   help="skip the platform reference figures (torch GEMM and sdpa)")
     p.add_argument("--graph", action="store_true",
                    help="replay the step (and the per-call loops) as captured HIP graphs instead of "
                         "launching every call from the host")
@@ -243,6 +255,216 @@ def stage_layers(w, layer_ids, dev):
     return layers
 
 
+def fused_applies(w, layers, two_calls: bool) -> bool:
+    """bsattn_select_forward ranks inside the attention kernel for bf16, D 64,
+    block 64, every block a candidate, at most 64 blocks, no head mask."""
+    return (not two_calls and w.dtype == "bf16" and w.D == 64 and w.block == 64 and not w.segments
+            and not w.window_tokens and w.nb <= 64 and w.budget < 1.0 and all(ly["hmd"] is None for ly in layers))
+
+
+class Run:
+    """One workload staged on the device, with its calls and timers."""
+
+    def __init__(self, w, dev, args, stack: bool, layer: int = 0):
+        self.w, self.dev, self.args = w, dev, args
+        self.layer_ids = list(range(w.layers)) if stack else [layer]
+        self.layers = stage_layers(w, self.layer_ids, dev)
+        self.layout = hm.Layout(w.block, list(w.segments), w.window_tokens)
+        _cls, self.n_cand = hm.layout_classes(self.layout, w.N)
+        L = len(self.layers)
+        self.bms = [hm.empty_block_mask(w.B, w.H, w.nb, dev) for _ in range(L)]
+        self.bm_full = hm.empty_block_mask(w.B, w.H, w.nb, dev)
+        self.ws = torch.empty(hm.select_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.block, w.D),
+                              dtype=torch.uint8, device=dev)
+        self.outs = [torch.empty_like(ly["qd"]) for ly in self.layers]
+        self.stream = torch.cuda.current_stream(dev)
+        self.timer = Timer(dev, self.stream, eager=not args.graph)
+        self.fused = fused_applies(w, self.layers, args.two_calls)
+
+    def select(self, i, st, budget=None, out=None):
+        ly = self.layers[i]
+        hm.select(ly["qd"], ly["kd"], self.layout, self.w.budget if budget is None else budget,
+                  out=self.bms[i] if out is None else out, workspace=self.ws, stream=st)
+
+    def forward(self, i, st, bm=None, head_mask="layer"):
+        ly = self.layers[i]
+        hmask = ly["hmd"] if isinstance(head_mask, str) else head_mask
+        hm.forward(ly["qd"], ly["kd"], ly["vd"], self.bms[i] if bm is None else bm, hmask, out=self.outs[i],
+                   stream=st)
+
+    def select_forward(self, i, st):
+        ly = self.layers[i]
+        hm.select_forward(ly["qd"], ly["kd"], ly["vd"], self.layout, self.w.budget, ly["hmd"], out=self.outs[i],
+                          block_mask=self.bms[i], workspace=self.ws, stream=st)
+
+    def two_call_step(self, st):
+        for i in range(len(self.layers)):
+            self.select(i, st)
+            self.forward(i, st)
+
+    def step(self, st):
+        """One pass of the hot path over the staged batch (every layer)."""
+        if not self.fused:
+            self.two_call_step(st)
+            return
+        for i in range(len(self.layers)):
+            self.select_forward(i, st)
+
+    def time_steps(self, steps: int, warmup: int, fn=None):
+        """Host-clocked ms per step over `steps` steps, synchronised on both sides."""
+        capture = fn is None and self.args.graph
+        fn = fn or (lambda: self.step(self.stream))
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        if capture:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream(self.dev)
+            cap.wait_stream(self.stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    self.step(cap)
+            self.stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            fn = graph.replay
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def kernel_figures(self, reps: int, warmup: int):
+        """Per-call figures on layer 0: attention roofline, selector GB/s,
+        speedup against the same kernel at full density."""
+        w, t = self.w, self.timer
+        sel_ms = t.warm(lambda st: self.select(0, st), reps, warmup)
+        sel_graph_ms = sel_ms if self.args.graph else Timer(self.dev, self.stream, eager=False).warm(
+            lambda st: self.select(0, st), reps, warmup)
+        fwd_ms = t.warm(lambda st: self.forward(0, st), reps, warmup)
+        self.select(0, self.stream, budget=1.0, out=self.bm_full)
+        dense_ms = t.warm(lambda st: self.forward(0, st, bm=self.bm_full), reps, warmup)
+        for i in range(len(self.layers)):      # the step's own masks, outside every timed region
+            self.select(i, self.stream)
+        torch.cuda.synchronize()
+        self.flops_layers = [kept_flops(self.bms[i].count, self.layers[i]["hmd"], w.block, w.D, w.H)
+                             for i in range(len(self.layers))]
+        flops0 = self.flops_layers[0]
+        flops_dense0 = kept_flops(self.bm_full.count, self.layers[0]["hmd"], w.block, w.D, w.H)
+        sel_bytes = selector_bytes(w, self.bms[0], self.n_cand)
+        attn_tflops = flops0 / (fwd_ms * 1e-3) / 1e12
+        sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
+        bf16 = w.dtype == "bf16"
+        roof = {"bound": "mfma", "kernel": "attn_mfma_kernel (bsattn_forward)" if bf16
+                else "attn_vec_kernel (bsattn_forward, fp32)",
+                "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": attn_tflops / (MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS),
+                "traffic": profiled_traffic(w.name) if bf16 else None,
+                "traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
+                "flops_per_launch": flops0, "avg_launch_ms": fwd_ms}
+        sel = {"bound": "hbm", "achieved": sel_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": sel_gbps / HBM_PEAK_GBPS, "bytes_per_call": sel_bytes, "avg_call_ms": sel_ms,
+               "graph_call_ms": sel_graph_ms,
+               "graph_frac": sel_bytes / (sel_graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "kernels": "pool_kernel + score_rank_kernel (bsattn_select)",
+               "note": "avg_call_ms: host-launched calls; graph_call_ms: the same calls replayed from a "
+                       "HIP graph (the kernels without the host's launch rate)"}
+        speed = {"attention": dense_ms / fwd_ms, "step": dense_ms / (min(sel_ms, sel_graph_ms) + fwd_ms),
+                 "dense_attention_ms": dense_ms, "dense_flops": flops_dense0, "ideal": flops_dense0 / flops0,
+                 "note": "attention: the same kernel at budget 1.0 over the 30 % launch; step: that dense "
+                         "launch over selector + attention (the selector's faster of host-launched and "
+                         "graph-replayed time)"}
+        return roof, sel, speed, fwd_ms
+
+    def radial_figures(self, reps, warmup):
+        w = self.w
+        bm_rad = hm.radial(self.layout, w.N, w.budget, B=1, H=1, device=self.dev)
+        rad_ms = self.timer.warm(lambda st: hm.radial(self.layout, w.N, w.budget, B=1, H=1, out=bm_rad, stream=st),
+                                 reps, warmup)
+        rad_fwd_ms = self.timer.warm(lambda st: self.forward(0, st, bm=bm_rad), reps, warmup)
+        torch.cuda.synchronize()
+        rad_flops = kept_flops(bm_rad.count, self.layers[0]["hmd"], w.block, w.D, w.H)
+        return {"radial_ms": rad_ms, "attention_ms": rad_fwd_ms, "flops": rad_flops,
+                "tflops": rad_flops / (rad_fwd_ms * 1e-3) / 1e12, "k": bm_rad.k,
+                "note": "bsattn_radial: the band at the selector's k (the control the selector has to beat); "
+                        "attention: bsattn_forward on the band"}
+
+    def head_mask_figures(self, fwd_ms, reps, warmup):
+        ly0 = self.layers[0]
+        if ly0["hmd"] is None:
+            return None
+        all_heads = torch.ones(self.w.H, dtype=torch.uint8, device=self.dev)
+        t_all = self.timer.warm(lambda st: self.forward(0, st, head_mask=all_heads), reps, warmup)
+        return {"active_heads": int(ly0["hm_np"].sum()), "heads": self.w.H, "all_heads_ms": t_all,
+                "masked_ms": fwd_ms, "time_skipped": 1.0 - fwd_ms / t_all,
+                "ideal_skipped": 1.0 - float(ly0["hm_np"].sum()) / self.w.H}
+
+    def sdpa_reference(self, reps):
+        """torch's own scaled_dot_product_attention (dense, bf16) on layer 0's
+        shape: the platform's flash attention, for context."""
+        w, ly = self.w, self.layers[0]
+        if w.dtype != "bf16":
+            return None
+        k, v = ly["kd"], ly["vd"]
+        if w.kv_heads != w.H:
+            k = k.repeat_interleave(w.H // w.kv_heads, dim=1)
+            v = v.repeat_interleave(w.H // w.kv_heads, dim=1)
+        fn = lambda st: torch.nn.functional.scaled_dot_product_attention(ly["qd"], k, v)
+        ms = self.timer.warm(fn, reps, 2)
+        fl = 4.0 * w.B * w.H * w.N * w.N * w.D
+        return {"ms": ms, "tflops": fl / ms / 1e9, "note": "torch sdpa, dense, all heads (context only)"}
+
+
+def gemm_reference(dev):
+    """bf16 GEMM rate of torch (hipBLASLt) at 8192^3: the platform's practical
+    matrix-core ceiling, for context."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    tf = 2.0 * n ** 3 / ms / 1e9
+    return {"gemm_bf16_8192_tflops": tf, "gemm_frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+
+
+def per_config_entry(w, dev, args):
+    """The figures of one configuration (its own step, kernels, controls)."""
+    stack = w.layers > 1
+    r = Run(w, dev, args, stack=stack)
+    steps = max(2, min(args.steps, 5 if stack else 20))
+    warmup = max(1, min(args.warmup, 2 if stack else 5))
+    ms_step = r.time_steps(steps, warmup)
+    reps = max(2, min(args.steps, 20))
+    roof, sel, speed, fwd_ms = r.kernel_figures(reps, min(args.warmup, 5))
+    flops = sum(r.flops_layers)
+    e = {"config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
+                    "block": w.block, "dtype": w.dtype, "budget": w.budget, "k": r.bms[0].k, "layers": w.layers,
+                    "segments": [list(s) for s in w.segments], "window_tokens": w.window_tokens},
+         "step": {"ms_per_step": ms_step, "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+                  "calls": "bsattn_select_forward" if r.fused else "bsattn_select + bsattn_forward",
+                  "layers_per_step": len(r.layers)},
+         "roofline": roof, "selector": sel, "speedup_vs_dense": speed}
+    if w.radial:
+        e["radial"] = r.radial_figures(reps, min(args.warmup, 5))
+    hmf = r.head_mask_figures(fwd_ms, reps, min(args.warmup, 5))
+    if hmf is not None:
+        e["head_masking"] = hmf
+    e["torch_sdpa_dense"] = r.sdpa_reference(3 if w.N > 20000 else 10)
+    del r
+    torch.cuda.empty_cache()
+    return e
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,138 +475,50 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     stack = w.layers > 1 and not args.one_layer
-    layer_ids = list(range(w.layers)) if stack else [args.layer]
-    layers = stage_layers(w, layer_ids, dev)
-
-    layout = hm.Layout(w.block, list(w.segments), w.window_tokens)
-    _cls, n_cand = hm.layout_classes(layout, w.N)
-    nb = w.nb
-    L = len(layers)
-    bms = [hm.empty_block_mask(w.B, w.H, nb, dev) for _ in range(L)]
-    bm_full = hm.empty_block_mask(w.B, w.H, nb, dev)
-    ws = torch.empty(hm.select_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.block, w.D),
-                     dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(ly["qd"]) for ly in layers]
-    stream = torch.cuda.current_stream(dev)
-    timer = Timer(dev, stream, eager=not args.graph)
-
-    def select(i, st, budget=None, out=None):
-        ly = layers[i]
-        hm.select(ly["qd"], ly["kd"], layout, w.budget if budget is None else budget,
-                  out=bms[i] if out is None else out, workspace=ws, stream=st)
-
-    def forward(i, st, bm=None):
-        ly = layers[i]
-        hm.forward(ly["qd"], ly["kd"], ly["vd"], bms[i] if bm is None else bm, ly["hmd"], out=outs[i], stream=st)
-
-    def select_forward(i, st):
-        ly = layers[i]
-        hm.select_forward(ly["qd"], ly["kd"], ly["vd"], layout, w.budget, ly["hmd"], out=outs[i],
-                          block_mask=bms[i], workspace=ws, stream=st)
-
-    def two_call_step(st):
-        for i in range(L):
-            select(i, st)
-            forward(i, st)
-
-    # The step is bsattn_select_forward: the same selection and attention,
-    # with the ranking inside the attention kernel where that kernel applies
-    # (bf16, D 64, block 64, every block a candidate, at most 64 blocks, no
-    # head mask), else the two calls.
-    fused = (not args.two_calls and w.dtype == "bf16" and w.D == 64 and w.block == 64 and not w.segments
-             and not w.window_tokens and w.nb <= 64 and w.budget < 1.0 and all(ly["hmd"] is None for ly in layers))
-
-    def step(st):
-        if not fused:
-            two_call_step(st)
-            return
-        for i in range(L):
-            select_forward(i, st)
+    r = Run(w, dev, args, stack=stack, layer=args.layer)
+    layers, L = r.layers, len(r.layers)
+    fused = r.fused
 
     # ---- whole-step throughput: K steps on the host clock, synchronised on
-    # both sides.  Every call is launched from the host (the host runs ahead
-    # of the GPU); --graph captures the step once and replays it instead.  On
+    # both sides.  The step is bsattn_select_forward where the fused kernel
+    # applies, else bsattn_select + bsattn_forward; every call is launched
+    # from the host (--graph captures the step once and replays it).  On
     # MI355X the replayed kernels start with a cold L2, so host launches are
     # the faster default here.
-    for _ in range(args.warmup):
-        step(stream)
-    torch.cuda.synchronize()
-    run_step = lambda: step(stream)
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                step(cap)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        run_step = graph.replay
-        for _ in range(args.warmup):
-            run_step()
-        torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = r.time_steps(args.steps, args.warmup)
     two_call_ms = None
     if fused and not args.graph:
-        # the same step as bsattn_select + bsattn_forward, for reference
-        for _ in range(args.warmup):
-            two_call_step(stream)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            two_call_step(stream)
-        torch.cuda.synchronize()
-        two_call_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        two_call_ms = r.time_steps(args.steps, args.warmup, fn=lambda: r.two_call_step(r.stream))
 
-    # ---- per-call figures (layer 0), warm: back-to-back calls in one graph
     reps = max(1, min(args.steps, 50))
-    sel_ms = timer.warm(lambda st: select(0, st), reps, args.warmup)
-    # the selector's kernels without the host's launch rate: the same calls
-    # captured in one HIP graph (short selections are host-bound launched
-    # one by one)
-    sel_graph_ms = sel_ms if args.graph else Timer(dev, stream, eager=False).warm(lambda st: select(0, st), reps,
-                                                                                    args.warmup)
-    fwd_ms = timer.warm(lambda st: forward(0, st), reps, args.warmup)
-    # the same attention kernel at full density (budget 1.0: same layout and head mask)
-    select(0, stream, budget=1.0, out=bm_full)
-    dense_ms = timer.warm(lambda st: forward(0, st, bm=bm_full), reps, args.warmup)
+    roof, sel, speed, fwd_ms = r.kernel_figures(reps, args.warmup)
+    flops = sum(r.flops_layers)
+    flops0 = r.flops_layers[0]
+
+    fused_fig = None
+    if fused:
+        # the step's own call, alone: pool (K only) + attention with the
+        # ranking inside; its rate counts the whole call (pool and ranking
+        # included) against the kept FLOPs
+        f_ms = r.timer.warm(lambda st: r.select_forward(0, st), reps, args.warmup)
+        f_graph_ms = Timer(dev, r.stream, eager=False).warm(lambda st: r.select_forward(0, st), reps, args.warmup)
+        fused_fig = {"call_ms": f_ms, "graph_call_ms": f_graph_ms,
+                     "tflops": flops0 / (f_ms * 1e-3) / 1e12,
+                     "frac": flops0 / (f_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "kernels": "pool_kernel (K only) + attn_mfma_kernel<FUSED> (bsattn_select_forward)",
+                     "note": "the step's calls; roofline and selector above are the two-call kernels "
+                             "(bsattn_forward, bsattn_select) on the same inputs"}
+
     # cold: L2 and MALL evicted before each call (secondary figures)
     cold = None
     if not args.no_cold:
         scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB
-        cold = {"selector_ms": timer.cold(lambda st: select(0, st), 11, scratch),
-                "attention_ms": timer.cold(lambda st: forward(0, st), 11, scratch),
+        cold = {"selector_ms": r.timer.cold(lambda st: r.select(0, st), 11, scratch),
+                "attention_ms": r.timer.cold(lambda st: r.forward(0, st), 11, scratch),
                 "note": "median of 11 single calls, each after a 512 MiB scratch write"}
         del scratch
 
-    # the step's own result, outside every timed region
-    for i in range(L):
-        select(i, stream)
-    torch.cuda.synchronize()
-    flops_layers = [kept_flops(bms[i].count, layers[i]["hmd"], w.block, w.D, w.H) for i in range(L)]
-    flops = sum(flops_layers)
-    flops0 = flops_layers[0]
-    flops_dense0 = kept_flops(bm_full.count, layers[0]["hmd"], w.block, w.D, w.H)
-    sel_bytes = selector_bytes(w, bms[0], n_cand)
-    attn_tflops = flops0 / (fwd_ms * 1e-3) / 1e12
-    sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
-
-    radial = None
-    if w.radial:
-        # the layout-only band control at the selector's density: the same k
-        bm_rad = hm.radial(layout, w.N, w.budget, B=1, H=1, device=dev)
-        rad_ms = timer.warm(lambda st: hm.radial(layout, w.N, w.budget, B=1, H=1, out=bm_rad, stream=st),
-                            reps, args.warmup)
-        rad_fwd_ms = timer.warm(lambda st: forward(0, st, bm=bm_rad), reps, args.warmup)
-        torch.cuda.synchronize()
-        rad_flops = kept_flops(bm_rad.count, layers[0]["hmd"], w.block, w.D, w.H)
-        radial = {"radial_ms": rad_ms, "attention_ms": rad_fwd_ms, "flops": rad_flops,
-                  "tflops": rad_flops / (rad_fwd_ms * 1e-3) / 1e12, "k": bm_rad.k}
+    radial = r.radial_figures(reps, args.warmup) if w.radial else None
 
     # per-token key mask composed with the block mask (bsattn_forward_masked):
     # all keys live, and the last 1/16 of each batch's keys masked
@@ -392,11 +526,14 @@ def main():
     km_tail = km_live.clone()
     km_tail[:, w.N - w.N // 16:] = 0
     ly0 = layers[0]
+    bms, outs = r.bms, r.outs
     key_mask = {
-        "all_live_ms": timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
-                                                        out=outs[0], stream=st, key_mask=km_live), reps, args.warmup),
-        "tail_masked_ms": timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
-                                                           out=outs[0], stream=st, key_mask=km_tail), reps, args.warmup),
+        "all_live_ms": r.timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
+                                                          out=outs[0], stream=st, key_mask=km_live),
+                                    reps, args.warmup),
+        "tail_masked_ms": r.timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], ly0["hmd"],
+                                                             out=outs[0], stream=st, key_mask=km_tail),
+                                       reps, args.warmup),
         "note": "bsattn_forward_masked on the step's block mask; tail = last N/16 keys of each batch masked",
     }
 
@@ -409,13 +546,14 @@ def main():
         k8, ks = hm.quantize_fp8(ly0["kd"])
         v8, vs = hm.quantize_fp8(ly0["vd"])
         out8 = torch.empty_like(outs[0])
-        quant_ms = timer.warm(lambda st: hm.quantize_fp8(ly0["qd"], out=q8, scale=qs, stream=st), reps, args.warmup)
-        fp8_ms = timer.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bms[0], ly0["hmd"], out=out8, stream=st),
-                            reps, args.warmup)
-        fp8_dense_ms = timer.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm_full, ly0["hmd"], out=out8,
-                                                            stream=st), reps, args.warmup)
-        fp8_km_ms = timer.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bms[0], ly0["hmd"], out=out8,
-                                                         stream=st, key_mask=km_tail), reps, args.warmup)
+        t = r.timer
+        quant_ms = t.warm(lambda st: hm.quantize_fp8(ly0["qd"], out=q8, scale=qs, stream=st), reps, args.warmup)
+        fp8_ms = t.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bms[0], ly0["hmd"], out=out8, stream=st),
+                        reps, args.warmup)
+        fp8_dense_ms = t.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, r.bm_full, ly0["hmd"], out=out8,
+                                                        stream=st), reps, args.warmup)
+        fp8_km_ms = t.warm(lambda st: hm.forward_fp8(q8, k8, v8, qs, ks, vs, bms[0], ly0["hmd"], out=out8,
+                                                     stream=st, key_mask=km_tail), reps, args.warmup)
         fp8_tf = flops0 / (fp8_ms * 1e-3) / 1e12
         fp8 = {"attention_ms": fp8_ms, "achieved": fp8_tf, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                "frac": fp8_tf / MFMA_FP8_PEAK_TFLOPS, "dense_attention_ms": fp8_dense_ms,
@@ -424,23 +562,18 @@ def main():
                "note": "bsattn_forward_fp8 on E4M3 Q/K/V with per-head scales (bf16 out); quantisation of one "
                        "[B,H,N,D] tensor timed separately; key_mask_tail: bsattn_forward_fp8_masked with the "
                        "last N/16 keys of each batch masked"}
+        del q8, k8, v8, out8
 
     # head masking: the same forward with every head active, for the share of
     # attention time the layer's head mask skips (the pages claim 50-70 %)
-    head_masking = None
-    if ly0["hmd"] is not None:
-        all_heads = torch.ones(w.H, dtype=torch.uint8, device=dev)
-        t_all = timer.warm(lambda st: hm.forward(ly0["qd"], ly0["kd"], ly0["vd"], bms[0], all_heads, out=outs[0],
-                                                 stream=st), reps, args.warmup)
-        head_masking = {"active_heads": int(ly0["hm_np"].sum()), "heads": w.H, "all_heads_ms": t_all,
-                        "masked_ms": fwd_ms, "time_skipped": 1.0 - fwd_ms / t_all}
+    head_masking = r.head_mask_figures(fwd_ms, reps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
         sample_ids = [0] if not stack else [0, w.layers // 3, 2 * w.layers // 3, w.layers - 1]
         sample = [(layers[i]["q"], layers[i]["k"], layers[i]["v"], layers[i]["hm_np"]) for i in sample_ids]
         # kept FLOPs of the sampled layers, so value compares like with like
-        flops_sample = sum(flops_layers[i] for i in sample_ids)
+        flops_sample = sum(r.flops_layers[i] for i in sample_ids)
         cpu = cpu_baseline(w, sample, flops_sample)
 
     if args.calibrate_copy:
@@ -451,6 +584,12 @@ def main():
         for _ in range(5):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
+
+    reference = {"note": "the platform's own kernels on this GPU, for context (not part of the path)"}
+    if not args.no_reference:
+        reference.update(gemm_reference(dev))
+        reference["torch_sdpa_dense_headline"] = r.sdpa_reference(10)
 
     hmask0 = layers[0]["hm_np"]
     res = {
@@ -472,24 +611,14 @@ def main():
         "two_call_ms_per_step": two_call_ms,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
                    "block": w.block, "budget": w.budget, "k": bms[0].k,
-                   "layers": L, "layer": layer_ids[0] if L == 1 else None,
+                   "layers": L, "layer": r.layer_ids[0] if L == 1 else None,
                    "segments": [list(s) for s in w.segments], "window_tokens": w.window_tokens,
                    "active_heads": int(hmask0.sum()) if hmask0 is not None else w.H,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel" if w.dtype == "bf16" else "attn_vec_kernel",
-                     "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(w.name),
-                     "traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
-                     "flops_per_launch": flops0, "avg_launch_ms": fwd_ms},
-        "selector": {"bound": "hbm", "achieved": sel_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": sel_gbps / HBM_PEAK_GBPS, "bytes_per_call": sel_bytes, "avg_call_ms": sel_ms,
-                     "graph_call_ms": sel_graph_ms,
-                     "graph_frac": sel_bytes / (sel_graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                     "note": "avg_call_ms: host-launched calls; graph_call_ms: the same calls replayed from a "
-                             "HIP graph (the kernels without the host's launch rate)"},
-        "speedup_vs_dense": {"attention": dense_ms / fwd_ms, "step": dense_ms / (sel_ms + fwd_ms),
-                             "dense_attention_ms": dense_ms, "dense_flops": flops_dense0,
-                             "ideal": flops_dense0 / flops0},
+        "roofline": roof,
+        "selector": sel,
+        "fused_step_call": fused_fig,
+        "speedup_vs_dense": speed,
         "cold": cold,
         "radial": radial,
         "key_mask": key_mask,
@@ -502,9 +631,22 @@ def main():
             "budget_30pct_vs_dense_before_after": [0.36, 1.19], "head_masking_compute_skipped_claim": [0.5, 0.7],
         },
         "cpu_baseline": cpu,
+        "reference": reference,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "host": platform.node()},
     }
+    del r, layers, bms, outs
+    torch.cuda.empty_cache()
+
+    # every configuration of the workload set, each with its own step,
+    # kernel figures and controls (the headline's entry is the line above)
+    if not args.no_per_config:
+        per = {}
+        for name in PER_CONFIG:
+            wc = workloads.ALL[name]
+            print(f"[bench] per-config {name}", file=sys.stderr, flush=True)
+            per[name] = per_config_entry(wc, dev, args)
+        res["per_config"] = per
     print(json.dumps(res), flush=True)
 
 

@@ -530,7 +530,7 @@ class Stage:
 
 def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, step: int = 0, head_mask=None,
                      key_mask=None, causal: bool = False, self_attention: bool = True, architecture=None,
-                     pipeline=None, denoiser=None, out=None, stream=None):
+                     pipeline=None, denoiser=None, out=None, block_mask: BlockMask | None = None, stream=None):
     """One attention call through the sparse stage (orchestration only).
 
     Asks the stage whether to serve the call; if it does, runs bsattn_select at
@@ -538,7 +538,8 @@ def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, ste
     carries a token key mask).  A declined self-attention call of a supported
     shape is computed dense by the same kernel (every block kept); a causal
     or cross-attention call returns None for the caller's own attention.
-    Returns (out or None, decision).
+    block_mask: optional caller buffer that receives a served call's
+    selection (otherwise a temporary).  Returns (out or None, decision).
     """
     has_layout = layout is not None and len(layout.segments) > 0
     d = stage.decide(q.shape[2], k.shape[2], step=step, self_attention=self_attention,
@@ -546,7 +547,7 @@ def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, ste
                      architecture=architecture, pipeline=pipeline, denoiser=denoiser)
     if d["outcome"] == STAGE_SPARSE:
         lay = layout if layout is not None else Layout(64, [])
-        bm = select(q, k, lay, d["budget"], stream=stream)
+        bm = select(q, k, lay, d["budget"], out=block_mask, stream=stream)
         out = forward(q, k, v, bm, head_mask, out=out, stream=stream,
                       key_mask=key_mask if d["use_key_mask"] else None)
         return out, d

@@ -73,6 +73,21 @@ def test_budget_rule_matches_oracle(lib):
     assert B_.budget_k(512, 0.3)[0] == 153 and B_.budget_k(63, 0.3)[0] == 18
 
 
+def test_budget_fraction_of_candidates_keeps_that_many(lib):
+    """bsattn_budget_k: the fraction k/n of n candidates keeps exactly k
+    (the double nearest k/n, and two-decimal budgets such as 0.29 of 100),
+    and a budget a hair below it keeps k - 1."""
+    for n in range(1, 257):
+        for k in range(1, n + 1):
+            assert B_.budget_k(n, k / n)[0] == k, (k, n)
+            if k > 1:
+                assert B_.budget_k(n, (k - 1e-6) / n)[0] == k - 1, (k, n)
+    for d in range(1, 100):
+        for n in (100, 200, 400, 800, 1500, 2000):
+            if d * n % 100 == 0:
+                assert B_.budget_k(n, d / 100)[0] == d * n // 100, (d, n)
+
+
 def test_head_mask_matches_oracle(lib):
     rng = np.random.default_rng(1)
     for trial in range(200):

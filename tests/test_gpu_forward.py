@@ -175,7 +175,7 @@ def test_forward_radial_mask_sampled(cuda, name):
     assert_close(got_rows, ref, "bf16", name + " radial")
 
 
-@pytest.mark.parametrize("layer", [0, 42])
+@pytest.mark.parametrize("layer", [0, 21, 42, 63])
 def test_forward_head_masked_stack_layer(cuda, layer):
     w = workloads.STACK
     q, k, v = workloads.make_qkv(w, layer)

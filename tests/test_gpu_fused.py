@@ -36,6 +36,9 @@ def check_fused(cuda, q, k, v, segs, block, budget, window=0, what=""):
     got = to64(out)
     keep_rows = np.repeat(tie == 0, block, axis=-1)
     assert_close(got[keep_rows], ref[keep_rows], "bf16", what)
+    # every row, near ties included: the attention over the call's own mask
+    own = oracle.attention(q64, k64, v64, block, download_mask(bm)[0])
+    assert_close(got, own, "bf16", what + " (own mask)")
     same = np.repeat((download_mask(bm)[0] == download_mask(bm_sep)[0]).all(-1), block, axis=-1)
     assert np.array_equal(got[same], to64(out_sep)[same])
     return got

@@ -15,7 +15,7 @@ import torch
 import head_masked_attention_amd as hm
 import oracle
 import workloads
-from parity import assert_close, to64, upload_mask
+from parity import assert_close, compare_masks, to64, upload_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +154,48 @@ def test_sparse_attention_through_the_stage(cuda):
     assert torch.equal(out2, hm.forward(qd, kd, vd))
     out3, d3 = hm.sparse_attention(qd, kd, vd, stage, lay, causal=True)
     assert out3 is None and d3["outcome"] == hm.DECLINE_CAUSAL
+
+
+def test_stage_schedule_against_the_oracle(cuda):
+    """sparse_attention over a two-value budget schedule with a token key
+    mask, each served step checked against the oracle: the block mask against
+    oracle.select at that step's budget (bit-exact outside near-tie rows), the
+    output against oracle.attention with the key mask on the GPU's own mask
+    (every row) and on the oracle's mask (rows without near ties).  A call the
+    stage declines as short is the oracle's dense attention with the key mask."""
+    segs = [("text", 100), ("padding", 60), ("image", 64 * 24 - 160)]
+    N = sum(n for _, n in segs)
+    B, H, D = 2, 3, 64
+    q, k, v = workloads.small_case(B=B, H=H, N=N, D=D, seed=41)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    rng = np.random.default_rng(42)
+    km = (rng.random((B, N)) > 0.05).astype(np.uint8)      # scattered masked keys
+    km[:, 100:160] = 0                                      # the padding tokens
+    km[1, N - 64 + 7:] = 0                                  # most of batch 1's last block
+    kmd = torch.from_numpy(km).to(cuda)
+    lay = hm.Layout(64, segs)
+    stage = hm.Stage(min_length=1024, n_steps=4, schedule=(0.5, 0.25, 2))
+    bm = hm.empty_block_mask(B, H, N // 64, cuda)
+    seen = set()
+    for step, budget in ((0, 0.5), (1, 0.5), (2, 0.25), (3, 0.25), (7, 0.25)):
+        out, d = hm.sparse_attention(qd, kd, vd, stage, lay, step=step, key_mask=kmd, block_mask=bm)
+        torch.cuda.synchronize()
+        assert d["outcome"] == hm.STAGE_SPARSE and d["budget"] == budget and d["use_key_mask"]
+        ref_mask, tie = oracle.select(q64, k64, 64, segs, budget)
+        compare_masks(bm, ref_mask, tie)
+        own = bm.mask.cpu().numpy()
+        got = to64(out)
+        assert_close(got, oracle.attention(q64, k64, v64, 64, own, key_mask=km), "bf16", f"step {step}")
+        rows = np.repeat(tie == 0, 64, axis=-1)
+        ref = oracle.attention(q64, k64, v64, 64, ref_mask, key_mask=km)
+        assert_close(got[rows], ref[rows], "bf16", f"step {step} oracle mask")
+        seen.add(budget)
+    assert seen == {0.5, 0.25}
+    # declined: shorter than the stage's minimum length -> dense with the key mask
+    short = hm.Stage(min_length=8192)
+    out, d = hm.sparse_attention(qd, kd, vd, short, lay, key_mask=kmd)
+    torch.cuda.synchronize()
+    assert d["outcome"] == hm.DECLINE_SHORT
+    ones = np.ones((N // 64, N // 64), np.uint8)
+    assert_close(to64(out), oracle.attention(q64, k64, v64, 64, ones, key_mask=km), "bf16", "declined short")

@@ -257,3 +257,20 @@ def test_select_and_forward_long_sequence(cuda):
     refo = oracle.attention(to64(q), to64(k), to64(v), 64, ref, rows=rows)
     got = out.cpu()[rows[:, 0], rows[:, 1], rows[:, 2]].double().numpy()
     assert_close(got, refo, "bf16", "long sequence")
+
+
+@pytest.mark.parametrize("D,nb,seed", [(32, 64, 60), (64, 64, 61), (128, 64, 62), (64, 256, 63), (128, 256, 64)])
+def test_select_zero_mean_half_budget(cuda, D, nb, seed):
+    """Zero-mean i.i.d. Q and K at a 50 % budget: every row's boundary sits at
+    the median score, near zero, where an error proportional to the summed
+    term magnitudes is largest against the score itself.  Many heads, masks
+    bit-exact outside near-tie rows; the fused call too where it applies."""
+    B, H = 1, 48 if nb == 64 else 12
+    q, k, v = workloads.small_case(B=B, H=H, N=64 * nb, D=D, seed=seed)
+    ref, tie = oracle_select(q, k, (), 64, 0.5)
+    bm = run_select(q.to(cuda), k.to(cuda), (), 64, 0.5)
+    compare_masks(bm, ref, tie)
+    if D == 64 and nb <= 64:
+        _out, bmf = hm.select_forward(q.to(cuda), k.to(cuda), v.to(cuda), hm.Layout(64, []), 0.5)
+        torch.cuda.synchronize()
+        compare_masks(bmf, ref, tie)

@@ -305,6 +305,24 @@ def test_diagonal_kept_and_rows_hold_exactly_k():
         assert np.all(mask.sum(-1) == kk)
 
 
+def test_budget_fraction_of_candidates_keeps_that_many():
+    """The budget is a fraction of the sparsifiable candidates (SD.Next
+    selector paragraph), so the fraction k/n of n candidates keeps exactly
+    k: for every 1 <= k <= n <= 512 with budget the double nearest k/n, and
+    for two-decimal budgets d/100 whenever d n / 100 is whole (0.29 of 100
+    candidates is 29, although 0.29 * 100 = 28.999999999999996 in doubles).
+    A budget a hair below k/n keeps k - 1: the budget is never exceeded."""
+    for n in range(1, 513):
+        for k in range(1, n + 1):
+            assert oracle.budget(n, k / n)[0] == k, (k, n)
+            if k > 1:
+                assert oracle.budget(n, (k - 1e-6) / n)[0] == k - 1, (k, n)
+    for d in range(1, 100):
+        for n in range(1, 2049):
+            if d * n % 100 == 0:
+                assert oracle.budget(n, d / 100)[0] == d * n // 100, (d, n)
+
+
 def test_full_budget_reports_dense_layout_only_mask():
     rng = np.random.default_rng(23)
     segs = [("text", 64), ("padding", 64), ("image", 512)]

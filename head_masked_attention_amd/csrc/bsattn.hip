@@ -145,8 +145,6 @@ bsattn_status check_mask_out(const bsattn_block_mask* m) {
     return BSATTN_OK;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
 
 extern "C" {
@@ -194,8 +192,8 @@ bsattn_status bsattn_budget_k(int32_t n_cand, double budget, int32_t* k, int32_t
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int32_t block,
                                      int64_t D) {
     if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || (block != 32 && block != 64)) return 0;
-    const size_t rows = (size_t)pooled_rows(N / block);   // >= pooled rows of any layout
-    return align256((size_t)B * H * rows * D * 4) + align256((size_t)B * Hkv * rows * D * 4);
+    // >= the pooled rows of any layout of this length
+    return pool_space(B, H, Hkv, pooled_rows(N / block), D).bytes;
 }
 
 }  // extern "C"
@@ -234,8 +232,9 @@ bsattn_status select_launch(const bsattn_tensor* q, const bsattn_tensor* k, cons
     if (g.is_dense) {
         e = launch_layout_fill(g, (int)(q->B * q->H), mo, s);
     } else {
-        float* qp = (float*)workspace;
-        float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
+        const PoolSpace ps = pool_space(q->B, q->H, k->H, pooled_rows(g.n_cand), q->D);
+        const PooledSums qp = pooled_part(workspace, ps.q_hi, ps.q_lo, ps.q_nrm);
+        const PooledSums kp = pooled_part(workspace, ps.k_hi, ps.k_lo, ps.k_nrm);
         // the XCD-grouped order when an XCD's share of the pooled Q and K fits
         // in its L2, where the attention launch that follows finds it
         const int64_t pooled_bytes = q->B * (q->H + k->H) * g.n_cand * layout->block * q->D *
@@ -277,7 +276,9 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
 // the symbol); the device address comes from hipGetSymbolAddress, taken once
 // per device with that device current.  Every call on one GPU shares the
 // array, so calls that overlap on one GPU race.  Nothing in it has to start
-// at zero: the pool kernel writes every sum the score kernel reads.
+// at zero: the pool kernel writes every sum and norm the score kernel reads
+// for the candidates (rows past them, the padding of a 16-row tile, only feed
+// score columns that are never ranked).
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) uint8_t scratch[BSATTN_NO_ALLOC_SCRATCH_BYTES];
 
@@ -535,11 +536,12 @@ bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor*
     mask->k = g.k;
     mask->is_dense = 0;
     // K's block sums only: each attention workgroup sums its own query block
-    float* kp = (float*)((char*)workspace + align256((size_t)q->B * q->H * pooled_rows(g.n_cand) * q->D * 4));
+    const PoolSpace ps = pool_space(q->B, q->H, k->H, pooled_rows(g.n_cand), q->D);
+    const PooledSums kp = pooled_part(workspace, ps.k_hi, ps.k_lo, ps.k_nrm);
     const int64_t pooled_bytes = q->B * k->H * g.n_cand * 64 * q->D * 2;
     const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
-    hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g, nullptr,
-                               kp, xcd_groups, s);
+    hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g,
+                               PooledSums{nullptr, nullptr, nullptr}, kp, xcd_groups, s);
     if (e != hipSuccess) return BSATTN_ERR_HIP;
     AttnArgs a{};
     a.q = view_of(q);
@@ -558,7 +560,8 @@ bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor*
     a.mH = 1;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     a.n_work = (int64_t)a.B * a.H * a.nqb;
-    a.kp = kp;
+    a.kp = kp.hi;
+    a.kp_lo = kp.lo;
     a.prow = (int32_t)pooled_rows(g.n_cand);
     a.keep = g.k;
     a.m_out = mask->mask;

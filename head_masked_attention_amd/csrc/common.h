@@ -36,6 +36,18 @@ __device__ __forceinline__ int64_t pooled_offset(int32_t p, int32_t d) {
     return (int64_t)(p >> 4) * 16 * D + ((c * 4 + gq) * 16 + li) * 4 + e;
 }
 
+// Block sums of one tensor (Q or K) in the selector workspace, per (b, head)
+// and candidate row: the float64 sum split into a float32 high part `hi` (in
+// the score MFMA's operand order, pooled_offset) and the float32 residual `lo`
+// (same order), so hi + lo carries the sum to about 2^-48 relative; and `nrm`,
+// an upper bound on the Euclidean norm of the row's hi part.  hi == NULL: the
+// tensor is not pooled.
+struct PooledSums {
+    float* hi;
+    float* lo;
+    float* nrm;
+};
+
 // Per-layout geometry, host-computed once per call and passed by value.
 struct Geometry {
     int32_t nb;          // blocks in the sequence (N / block)

@@ -22,7 +22,8 @@ struct AttnArgs {
     // fused selection (bsattn_select_forward): the selector's pooled key
     // sums (each workgroup sums its own query block), the candidates kept
     // per row, and the block mask written out
-    const float* kp;             // [B][Hkv][prow][D], NULL in the plain forward
+    const float* kp;             // [B][Hkv][prow][D] hi parts, NULL in the plain forward
+    const float* kp_lo;          // ... and their float32 residuals (same layout)
     int32_t prow;                // pooled rows per head
     int32_t keep;                // k
     uint8_t* m_out;
@@ -30,14 +31,39 @@ struct AttnArgs {
     int32_t* i_out;
 };
 
+// Selector workspace: PooledSums of Q ([B][H] heads) then of K ([B][Hkv]
+// heads), `rows` candidate rows per head, D dimensions; every part 256-byte
+// aligned.  Offsets in bytes from the workspace base.
+struct PoolSpace {
+    size_t q_hi, k_hi, q_lo, k_lo, q_nrm, k_nrm, bytes;
+};
+__host__ inline size_t align_up256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ inline PoolSpace pool_space(int64_t B, int64_t H, int64_t Hkv, int64_t rows, int64_t D) {
+    PoolSpace ps;
+    const size_t qs = align_up256((size_t)B * H * rows * D * 4), ks = align_up256((size_t)B * Hkv * rows * D * 4);
+    const size_t qn = align_up256((size_t)B * H * rows * 4), kn = align_up256((size_t)B * Hkv * rows * 4);
+    ps.q_hi = 0;
+    ps.k_hi = qs;
+    ps.q_lo = qs + ks;
+    ps.k_lo = 2 * qs + ks;
+    ps.q_nrm = 2 * (qs + ks);
+    ps.k_nrm = 2 * (qs + ks) + qn;
+    ps.bytes = 2 * (qs + ks) + qn + kn;
+    return ps;
+}
+__host__ inline PooledSums pooled_part(void* ws, size_t hi, size_t lo, size_t nrm) {
+    char* b = (char*)ws;
+    return PooledSums{(float*)(b + hi), (float*)(b + lo), (float*)(b + nrm)};
+}
+
 // xcd_groups: the selector's two launches take their work in the attention
 // kernel's XCD-grouped (b, K/V head) order, so that pooled sums, masks and
 // lists are written by the XCD whose attention workgroups read them next
 // (chosen by the host when an XCD's share of Q and K fits in its L2).
-// qp NULL: pool K only.
+// qp.hi NULL: pool K only.
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s);
-hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
+                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s);
+hipError_t launch_score_rank(int D, PooledSums qp, PooledSums kp, int B, int H, int Hkv,
                              const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s);
 hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
 // bf16, D 64, block 64, every block a candidate (nkb <= 64), no head or key

@@ -30,6 +30,20 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
     }
 }
 
+// lane_xor of a float64 (its two 32-bit halves exchanged the same way).
+__device__ __forceinline__ double lane_xor_f64(double x, int m) {
+    const uint64_t u = __double_as_longlong(x);
+    const uint32_t lo = lane_xor((uint32_t)u, m), hi = lane_xor((uint32_t)(u >> 32), m);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Order-preserving map of a float64 to uint64 (-0 taken as +0).
+__device__ __forceinline__ uint64_t orderable64(double f) {
+    uint64_t u = (uint64_t)__double_as_longlong(f);
+    if ((u << 1) == 0) u = 0;                       // -0 -> +0
+    return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
 // Order-preserving map of a float to uint32 (-0 taken as +0).
 __device__ __forceinline__ uint32_t orderable(float f) {
     uint32_t u = __float_as_uint(f);

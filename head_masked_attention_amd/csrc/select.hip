@@ -44,11 +44,13 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // kernel, so that the XCD that pools a group's Q and K is the one whose
 // attention workgroups read them next, from its L2 when an XCD's share fits
 // there (the host decides).  Otherwise the plain order (tensor, b, head,
-// block).  qp NULL: K only (the fused attention sums its own query block).
+// block).  qp.hi NULL: K only (the fused attention sums its own query block).
+// The sums are taken in float64 (exact for bf16 inputs short of extreme
+// exponent spreads) and stored as PooledSums: float32 hi and lo parts and a
+// norm bound of the hi row, which the score kernel's error bound uses.
 template <typename T, int D, int BLOCK>
 __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int H, int Hkv,
-                                                   Geometry g, float* __restrict__ qp,
-                                                   float* __restrict__ kp, int xcd_groups) {
+                                                   Geometry g, PooledSums qp, PooledSums kp, int xcd_groups) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per token row
     constexpr int RPI = 64 / CPR;              // token rows per wave instruction
@@ -60,7 +62,8 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     // 32-bit index arithmetic (the host checks that the items fit): the
     // division sequences sit in front of every wavefront's loads
     const uint32_t nc = (uint32_t)g.n_cand;
-    const uint32_t nq = qp == nullptr ? 0u : (uint32_t)B * (uint32_t)H * nc, nk = (uint32_t)B * (uint32_t)Hkv * nc;
+    const bool with_q = qp.hi != nullptr;
+    const uint32_t nq = with_q ? (uint32_t)B * (uint32_t)H * nc : 0u, nk = (uint32_t)B * (uint32_t)Hkv * nc;
     // which tensor, (b, head) and candidate this wavefront pools; the
     // tensor's fields are selected by value (a pointer to a kernel argument
     // would put both views in scratch memory)
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     if (xcd_groups) {
         const uint32_t item = (uint32_t)xcd_logical_id(blockIdx.x, gridDim.x) * 4u + wave;   // grid: a multiple of 8
         if (item >= nq + nk) return;
-        const uint32_t rep = qp == nullptr ? 0u : (uint32_t)(H / Hkv);
+        const uint32_t rep = with_q ? (uint32_t)(H / Hkv) : 0u;
         const uint32_t per_group = (rep + 1) * nc;
         const uint32_t grp = item / per_group, r = item - grp * per_group;
         b = grp / (uint32_t)Hkv;
@@ -97,10 +100,10 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     const T* src_p = (const T*)(is_q ? q.p : k.p);
     const int64_t sb = is_q ? q.sb : k.sb, sh = is_q ? q.sh : k.sh, sn = is_q ? q.sn : k.sn;
     const int64_t heads = is_q ? H : Hkv;
-    float* out = is_q ? qp : kp;
+    const PooledSums out = is_q ? qp : kp;
 
     const int64_t blk = cand_block(g, (int32_t)p);
-    float* dst = out + ((int64_t)b * heads + hh) * pooled_rows(g.n_cand) * D;
+    const int64_t head_row0 = ((int64_t)b * heads + hh) * pooled_rows(g.n_cand);
 
     const T* base = src_p + b * sb + hh * sh + (blk * BLOCK + lane / CPR) * sn + (lane % CPR) * EPC;
     uint4 raw[NL];
@@ -108,35 +111,51 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
     for (int l = 0; l < NL; ++l)
         raw[l] = *(const uint4*)(base + (int64_t)l * RPI * sn);
 
-    float acc[EPC];
+    double acc[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
         const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += __uint_as_float(w[e] << 16);
-                acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+                acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+                acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+            for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(w[e]);
         }
     }
     // lanes holding the same chunk of different rows: lane % CPR equal
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += __uint_as_float(lane_xor(__float_as_uint(acc[e]), off));
+        for (int e = 0; e < EPC; ++e) acc[e] += lane_xor_f64(acc[e], off);
 
+    // every lane now holds its chunk's sums; split them, and sum the squares
+    // of the hi parts over the row's CPR chunks (lanes 0 .. CPR - 1)
+    float hi[EPC], lo[EPC];
+    double n2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+        hi[e] = (float)acc[e];
+        lo[e] = (float)(acc[e] - (double)hi[e]);
+        n2 += (double)hi[e] * (double)hi[e];
+    }
+#pragma unroll
+    for (int off = 1; off < CPR; off <<= 1) n2 += lane_xor_f64(n2, off);
     if (lane < CPR) {
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-            *(f4v*)(dst + pooled_offset<D>((int32_t)p, lane * EPC + e)) =
-                f4v{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        for (int e = 0; e < EPC; e += 4) {
+            const int64_t o = head_row0 * D + pooled_offset<D>((int32_t)p, lane * EPC + e);
+            *(f4v*)(out.hi + o) = f4v{hi[e], hi[e + 1], hi[e + 2], hi[e + 3]};
+            *(f4v*)(out.lo + o) = f4v{lo[e], lo[e + 1], lo[e + 2], lo[e + 3]};
+        }
     }
+    // rounded up: an upper bound of the norm
+    if (lane == 0) out.nrm[head_row0 + p] = (float)(sqrt(n2) * (1.0 + 0x1p-20));
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
@@ -260,6 +279,53 @@ __device__ __forceinline__ const int16_t* fill_codes(const Geometry& g, int16_t*
     return table;
 }
 
+// Float64 dot product of two candidate rows' (hi + lo) block sums (row p of
+// the query head's sums, row pos of the key head's), four partial sums so
+// the loads of an unrolled group issue together and the FMA chains overlap.
+template <int D>
+__device__ __forceinline__ double pooled_dot64(const float* qhi, const float* qlo, const float* khi,
+                                               const float* klo, int p, int pos) {
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int c = 0; c < D / 4; ++c) {
+        const int64_t oq = pooled_offset<D>(p, 4 * c), ok = pooled_offset<D>(pos, 4 * c);
+        const f4v qh = *(const f4v*)(qhi + oq), ql = *(const f4v*)(qlo + oq);
+        const f4v kh = *(const f4v*)(khi + ok), kl = *(const f4v*)(klo + ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            t[e] = fma((double)qh[e] + (double)ql[e], (double)kh[e] + (double)kl[e], t[e]);
+    }
+    return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+// A row ranked from float64 scores: for every candidate but the diagonal,
+// the dot product of the (hi + lo) block sums in float64; keys are the
+// order-preserving image of that score with its low index bits replaced by
+// the reversed candidate position (relative resolution 2^-41), the diagonal
+// first; one wavefront sorts them (64-bit bitonic) and marks the first
+// `keep` in keep_row (cleared by the caller).  The slow, exact path taken by
+// the rows whose float32 ranking could not be certified.
+template <int D, int E>
+__device__ __noinline__ void exact_rank(const float* qhi, const float* qlo, const float* khi, const float* klo,
+                                        int p, int n_cand, int keep, int lane, uint8_t* keep_row) {
+    constexpr int NPAD = 64 * E;
+    constexpr uint64_t IM = (uint64_t)NPAD - 1;
+    uint64_t key[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int pos = lane * E + r;
+        const uint64_t low = IM - (uint64_t)pos;
+        const double acc = pos < n_cand && pos != p ? pooled_dot64<D>(qhi, qlo, khi, klo, p, pos) : 0.0;
+        if (pos >= n_cand) key[r] = 0ull;
+        else if (pos == p) key[r] = ~IM | low;
+        else key[r] = (orderable64(acc) & ~IM) | low;
+    }
+    wave_bitonic_desc<E>(key, lane);
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+        if (lane * E + r < keep) keep_row[IM - (key[r] & IM)] = 1;
+}
+
 // Rows per workgroup and wavefronts per workgroup of the score/rank kernel:
 // one 16-row MFMA tile per workgroup (more workgroups beat longer ones:
 // 32-row tiles took 32 -> 26 us on the joint text+image shape and 100 -> 70 us
@@ -300,7 +366,7 @@ struct RankShape {
 // ---------------------------------------------------------------------------
 template <int D, int E>
 __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kernel(
-    const float* __restrict__ qp, const float* __restrict__ kp, int B, int H, int Hkv, Geometry g,
+    PooledSums qp, PooledSums kp, int B, int H, int Hkv, Geometry g,
     MaskOut out, int n_tiles, int xcd_groups) {
     constexpr int NPAD = 64 * E;
     constexpr int RT = RankShape<D, E>::RT;
@@ -337,8 +403,20 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
     if (threadIdx.x < RT) s_rowblk[threadIdx.x] = cand_block(g, p0 + (int)threadIdx.x);
 
     const int64_t prow = pooled_rows(g.n_cand);
-    const float* qbase = qp + bh * prow * D;
-    const float* kbase = kp + (b * Hkv + g_kv) * prow * D;
+    const float* qbase = qp.hi + bh * prow * D;
+    const float* kbase = kp.hi + (b * Hkv + g_kv) * prow * D;
+    const float* qlo = qp.lo + bh * prow * D;
+    const float* klo = kp.lo + (b * Hkv + g_kv) * prow * D;
+    // the largest key-row norm of this (b, K/V head), for the error bound of
+    // the float32 scores (each wavefront reduces it on its own)
+    float kmax = 0.f;
+    {
+        const float* kn = kp.nrm + (b * Hkv + g_kv) * prow;
+        for (int j = lane; j < g.n_cand; j += 64) kmax = fmaxf(kmax, kn[j]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) kmax = fmaxf(kmax, __uint_as_float(lane_xor(__float_as_uint(kmax), off)));
+    }
+    const float* qnrm = qp.nrm + bh * prow;
 
     // ---- scores S[p0 + r][c] = <Qsum_(p0+r), Ksum_c> with fp32 MFMA 16x16x4;
     // operands come straight from the tiled sums (1 KB per wave read)
@@ -391,6 +469,119 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
                     });
     };
 
+    // Marks the kept candidates of one row in keep_row (cleared by the
+    // caller) from this wavefront's sorted keys.  pos_of(r): candidate
+    // position of the lane's r-th key (ranks lane * E + r, descending);
+    // score_at(rank): the float32 score at that rank; tb: the keys resolve
+    // scores to 2^-tb relative (0: exact float32 scores).
+    //
+    // Every float32 score is within err = (2 D + 16) 2^-24 |Q_i| max_j |K_j|
+    // of the exact block-sum score (the float32 MFMA's accumulation and the
+    // hi/lo split, bounded through the norms), and the sort sees it to within
+    // T = 2^(1 - tb) max(|a|, |b|), where a and b are the scores at ranks k - 1
+    // (last kept) and k (first dropped).  If a - b > M = 2 err + 2 T, every
+    // kept candidate's exact score exceeds every dropped one's: the sort's
+    // top k is the exact top k.  Otherwise a candidate scoring above a + M is
+    // certainly kept, one below b - M certainly dropped, and the remaining
+    // slots go to the best of the band between, ranked by float64 scores of
+    // the (hi + lo) sums with ties to the lower block (a band of more than 64
+    // ranks the whole row in float64).  Nothing to rank when k < 2 (the
+    // diagonal alone) or every candidate is kept.
+    __shared__ int16_t s_band[WAVES][64];
+    __shared__ double s_bandt[WAVES][64];
+    auto select_row = [&](auto score_at, auto pos_of, int p, int rl, int tb, float qn, uint8_t* keep_row) {
+        auto mark_sorted = [&]() {
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (lane * E + r < g.k) keep_row[pos_of(r)] = 1;
+        };
+        if (g.k < 2 || g.k >= g.n_cand) { mark_sorted(); return; }
+        const float a = score_at(g.k - 1), b = score_at(g.k);
+        const float err = (float)(2 * D + 16) * 0x1p-24f * qn * kmax + 0x1p-100f;
+        const float T = tb ? ldexpf(fmaxf(fabsf(a), fabsf(b)), 1 - tb) : 0.f;
+        const float M = 2.f * err + 2.f * T;
+        if (a - b > M) { mark_sorted(); return; }
+        const float hi_edge = a + M, lo_edge = b - M;
+        const float* srow = s_score + rl * SSTR;
+        const uint64_t below = (1ull << lane) - 1ull;
+        int n_in = 0, m = 0;
+        bool band[E];
+        int pos[E];
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            pos[r] = pos_of(r);
+            // ranks past the candidates hold the padding keys
+            const bool real = lane * E + r < g.n_cand && pos[r] != p;
+            const float sc = srow[real ? pos[r] : 0];
+            const bool in = real && sc > hi_edge;
+            band[r] = real && !in && sc >= lo_edge;
+            n_in += __popcll(__ballot(in));
+            m += __popcll(__ballot(band[r]));
+            if (in) keep_row[pos[r]] = 1;
+        }
+        if (lane == 0) keep_row[p] = 1;                     // the diagonal
+        if (m > 64) {
+            // a wide band: the whole row from float64 scores
+#pragma unroll
+            for (int r = 0; r < E; ++r) keep_row[lane * E + r] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            exact_rank<D, E>(qbase, qlo, kbase, klo, p, g.n_cand, g.k, lane, keep_row);
+            return;
+        }
+        // the band's positions, one per lane
+        int base = 0;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            const uint64_t bal = __ballot(band[r]);
+            if (band[r]) s_band[wave][base + __popcll(bal & below)] = (int16_t)pos[r];
+            base += __popcll(bal);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // float64 scores of the band, four candidates at a time, sixteen lanes
+        // each (a lane takes a quarter-row slice of 4-dimension groups, so
+        // all its loads issue together), summed across the sixteen lanes
+        constexpr int G4 = D / 4, PER = (G4 + 15) / 16;
+        for (int c0 = 0; c0 < m; c0 += 4) {
+            const int cb = c0 + (lane >> 4), sl = lane & 15;
+            double t = 0.0;
+            if (cb < m) {
+                const int pos = s_band[wave][cb];
+#pragma unroll
+                for (int u = 0; u < PER; ++u) {
+                    const int gi = sl + 16 * u;
+                    if (gi < G4) {
+                        const int64_t oq = pooled_offset<D>(p, 4 * gi), ok = pooled_offset<D>(pos, 4 * gi);
+                        const f4v qh = *(const f4v*)(qbase + oq), ql = *(const f4v*)(qlo + oq);
+                        const f4v kh = *(const f4v*)(kbase + ok), kl = *(const f4v*)(klo + ok);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            t = fma((double)qh[e] + (double)ql[e], (double)kh[e] + (double)kl[e], t);
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) t += lane_xor_f64(t, off);
+            if (sl == 0 && cb < m) s_bandt[wave][cb] = t;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int my_pos = lane < m ? (int)s_band[wave][lane] : 0;
+        const double t = lane < m ? s_bandt[wave][lane] : 0.0;
+        // rank within the band: better = higher score, then lower block
+        const uint64_t tu = (uint64_t)__double_as_longlong(t);
+        int ahead = 0;
+        for (int i = 0; i < m; ++i) {
+            const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)tu, i);
+            const uint32_t hi32 = __builtin_amdgcn_readlane((uint32_t)(tu >> 32), i);
+            const int pi = __builtin_amdgcn_readlane(my_pos, i);
+            const double ti = __longlong_as_double((long long)(((uint64_t)hi32 << 32) | lo32));
+            ahead += (ti > t || (ti == t && pi < my_pos)) ? 1 : 0;
+        }
+        if (lane < m && ahead < (g.k - 1) - n_in) keep_row[my_pos] = 1;
+    };
+
     if constexpr (K32) {
         // ---- RR rows at a time per wavefront
         constexpr int IB = __builtin_ctz(NPAD);            // index bits
@@ -412,6 +603,10 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
                     key[q][r] = kv;
                 }
             }
+            // the rows' query norms, loaded while the keys sort
+            float qn[RR];
+#pragma unroll
+            for (int q = 0; q < RR; ++q) qn[q] = qnrm[min(p0 + r0 + q, g.n_cand - 1)];
             wave_bitonic_desc32<RR, E>(key, lane);
 #pragma unroll
             for (int q = 0; q < RR; ++q)
@@ -420,10 +615,22 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int q = 0; q < RR; ++q)
+            for (int q = 0; q < RR; ++q) {
+                if (r0 + q >= rows) continue;
+                // the float32 scores at ranks k - 1 (last kept) and k (first
+                // dropped), from the positions in the sorted keys
+                auto score_at = [&](int rank) -> float {
+                    uint32_t kv = 0u;
 #pragma unroll
-                for (int r = 0; r < E; ++r)
-                    if (lane * E + r < g.k && r0 + q < rows) s_keep[wave][q][IMASK - (key[q][r] & IMASK)] = 1;
+                    for (int r = 0; r < E; ++r)
+                        if (r == rank % E) kv = key[q][r];
+                    kv = __builtin_amdgcn_readlane(kv, rank / E);
+                    return s_score[(r0 + q) * SSTR + (int)(IMASK - (kv & IMASK))];
+                };
+                auto pos_of = [&](int r) -> int { return (int)(IMASK - (key[q][r] & IMASK)); };
+                // the kept bits of a 32-bit key resolve scores to 2^-(23 - IB)
+                select_row(score_at, pos_of, p0 + r0 + q, r0 + q, 23 - IB, qn[q], s_keep[wave][q]);
+            }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -445,14 +652,22 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
                 else if (pos == p) key[r] = (0xffffffffull << 32) | low;
                 else key[r] = ((uint64_t)orderable(s_score[rl * SSTR + pos]) << 32) | low;
             }
+            const float qn = qnrm[p];
             wave_bitonic_desc<E>(key, lane);
 #pragma unroll
             for (int r = 0; r < E; ++r) s_keep[wave][0][lane * E + r] = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            auto score_at = [&](int rank) -> float {
+                uint64_t kv = 0ull;
 #pragma unroll
-            for (int r = 0; r < E; ++r)
-                if (lane * E + r < g.k) s_keep[wave][0][0xffffffffu - (uint32_t)key[r]] = 1;
+                for (int r = 0; r < E; ++r)
+                    if (r == rank % E) kv = key[r];
+                const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)kv, rank / E);
+                return s_score[rl * SSTR + (int)(0xffffffffu - lo32)];
+            };
+            auto pos_of = [&](int r) -> int { return (int)(0xffffffffu - (uint32_t)key[r]); };
+            select_row(score_at, pos_of, p, rl, 0, qn, s_keep[wave][0]);
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
             compact_sparse(p, s_keep[wave][0]);
@@ -518,8 +733,8 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
-                                const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s) {
-    const int64_t items = (int64_t)B * ((qp == nullptr ? 0 : H) + Hkv) * g.n_cand;
+                                const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s) {
+    const int64_t items = (int64_t)B * ((qp.hi == nullptr ? 0 : H) + Hkv) * g.n_cand;
     const int64_t wgs = (items + 3) / 4;
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
     if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
@@ -527,7 +742,7 @@ static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int H
 }
 
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, float* qp, float* kp, int xcd_groups, hipStream_t s) {
+                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s) {
     if (dtype_is_f32) {
         if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
         if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
@@ -539,7 +754,7 @@ hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int
 }
 
 template <int D, int E>
-static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H, int Hkv,
+static hipError_t launch_score_t(PooledSums qp, PooledSums kp, int B, int H, int Hkv,
                                  const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
     constexpr int RT = RankShape<D, E>::RT;
     const int n_tiles = (g.n_cand + RT - 1) / RT;
@@ -550,7 +765,7 @@ static hipError_t launch_score_t(const float* qp, const float* kp, int B, int H,
 }
 
 template <int D>
-static hipError_t launch_score_d(const float* qp, const float* kp, int B, int H, int Hkv,
+static hipError_t launch_score_d(PooledSums qp, PooledSums kp, int B, int H, int Hkv,
                                  const Geometry& g, MaskOut out, int xg, hipStream_t s) {
     const int n = g.n_cand;
     if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, xg, s);
@@ -561,7 +776,7 @@ static hipError_t launch_score_d(const float* qp, const float* kp, int B, int H,
     return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, xg, s);
 }
 
-hipError_t launch_score_rank(int D, const float* qp, const float* kp, int B, int H, int Hkv,
+hipError_t launch_score_rank(int D, PooledSums qp, PooledSums kp, int B, int H, int Hkv,
                              const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
     if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
     if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);

@@ -166,9 +166,10 @@ bsattn_status bsattn_layout_classes(const bsattn_layout* layout, int64_t N,
 bsattn_status bsattn_budget_k(int32_t n_cand, double budget, int32_t* k, int32_t* is_dense);
 
 /*
- * Workspace bytes bsattn_select needs (device memory, 256-byte aligned):
- * fp32 block sums of Q and K for the sparsifiable blocks.  An upper bound
- * that holds for every layout with these sizes.
+ * Workspace bytes bsattn_select needs (device memory, 256-byte aligned): the
+ * block sums of Q and K for the sparsifiable blocks, taken in float64 and
+ * kept as float32 high and low parts, plus a norm bound per block.  An upper
+ * bound that holds for every layout with these sizes.
  */
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N,
                                      int32_t block, int64_t D);
@@ -184,6 +185,12 @@ size_t bsattn_select_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t 
  *  candidates (higher score first, ties to the lower block index), OR the
  *  sliding window, then apply pins and drops.  PINNED rows keep every
  *  non-dropped column; DROPPED rows and columns are empty.
+ *  The kept set follows the exact scores: block sums are taken in float64;
+ *  each row is ranked on float32 scores and kept as ranked only when the gap
+ *  at the budget boundary exceeds a bound on their rounding error, otherwise
+ *  the candidates near the boundary are ranked again by float64 scores.
+ *  Only scores within about 2^-40 of each other (relative to the summed term
+ *  magnitudes) can order differently from exact arithmetic.
  *  out: B == q->B, H == q->H, nqb == nkb == N / block; mask, count and index
  *  fully written.  out->k and out->is_dense are set before returning.
  *  When is_dense, no scoring runs and the layout-only mask is written.
@@ -210,7 +217,7 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
  * contents: calls that overlap on one GPU (several streams, several host
  * threads) race and must be ordered by the caller.
  */
-#define BSATTN_NO_ALLOC_SCRATCH_BYTES (16u << 20)
+#define BSATTN_NO_ALLOC_SCRATCH_BYTES (32u << 20)
 bsattn_status bsattn_select_no_alloc(const bsattn_tensor* q, const bsattn_tensor* k,
                                      const bsattn_layout* layout, double budget,
                                      bsattn_block_mask* out, void* stream);
@@ -265,11 +272,11 @@ bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
  *  wavefront -- bf16, D 64, block 64, no layout segments, no window, at most
  *  64 blocks, a budget that keeps fewer than all of them, no head mask --
  *  two kernels run: the block pooling of K, then one attention kernel whose
- *  workgroups sum their own query block and rank their own rows (the query
- *  sums equal the pooled ones bit for bit; the selector's keys and sort, so the
- *  same masks up to near-ties within 2^-14 relative, where the two fp32
- *  summation orders may differ) and attend over the kept blocks; otherwise
- *  the two calls run as written.  Enqueues only; never synchronises.
+ *  workgroups sum their own query block and rank their own rows from float64
+ *  scores (resolved to 2^-17 relative: the same masks as bsattn_select
+ *  except where two scores lie that close) and attend over the kept blocks;
+ *  otherwise the two calls run as written.  Enqueues only; never
+ *  synchronises.
  */
 bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor* k,
                                     const bsattn_tensor* v, const bsattn_layout* layout,

@@ -170,10 +170,10 @@ def test_select_no_alloc_validation(lib):
                                         args["budget"], ctypes.byref(args["out"]), None)
         assert st == code, (over, st)
         assert args["out"].k == -7
-    # 64 heads x 1024 blocks x D 128: 64 MiB of pooled sums, over the 16 MiB scratch
+    # 64 heads x 1024 blocks x D 128: 128 MiB of pooled sums, over the 32 MiB scratch
     big = tensor(H=64, N=64 * 1024, D=128)
     out = bmask(H=64, nb=1024)
-    assert B_.select_workspace_bytes(1, 64, 64, 64 * 1024, 64, 128) > 16 << 20
+    assert B_.select_workspace_bytes(1, 64, 64, 64 * 1024, 64, 128) > 32 << 20
     st = lib.bsattn_select_no_alloc(ctypes.byref(big), ctypes.byref(big), ctypes.byref(lay), 0.3,
                                     ctypes.byref(out), None)
     assert st == 7 and out.k == -7
@@ -319,7 +319,15 @@ def test_head_mask_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    assert B_.select_workspace_bytes(2, 10, 10, 4096, 64, 64) == 2 * 2 * 10 * 64 * 64 * 4
-    assert B_.select_workspace_bytes(1, 4, 2, 512, 32, 32) == 256 * ((4 * 16 * 32 * 4 + 255) // 256) + \
-        256 * ((2 * 16 * 32 * 4 + 255) // 256)
+    # per tensor: float32 hi and lo parts of the block sums ([heads][rows][D]
+    # each) and one float norm bound per row; every part 256-byte aligned
+    def a256(x):
+        return 256 * ((x + 255) // 256)
+
+    def expect(B, H, Hkv, rows, D):
+        return 2 * (a256(B * H * rows * D * 4) + a256(B * Hkv * rows * D * 4)) + \
+            a256(B * H * rows * 4) + a256(B * Hkv * rows * 4)
+    assert B_.select_workspace_bytes(2, 10, 10, 4096, 64, 64) == expect(2, 10, 10, 64, 64)
+    assert B_.select_workspace_bytes(2, 10, 10, 4096, 64, 64) == 2 * 2 * 2 * 10 * 64 * 64 * 4 + 2 * 2 * 10 * 64 * 4
+    assert B_.select_workspace_bytes(1, 4, 2, 512, 32, 32) == expect(1, 4, 2, 16, 32)
     assert B_.select_workspace_bytes(1, 1, 1, 512, 48, 32) == 0

@@ -274,3 +274,60 @@ def test_select_zero_mean_half_budget(cuda, D, nb, seed):
         _out, bmf = hm.select_forward(q.to(cuda), k.to(cuda), v.to(cuda), hm.Layout(64, []), 0.5)
         torch.cuda.synchronize()
         compare_masks(bmf, ref, tie)
+
+
+def cancellation_case(D, nb, H, seed):
+    """bf16 Q/K whose block scores are exact small values reached through
+    large cancelling terms.  Every query token is all ones; every token of
+    key block j of head h is R_h + s_j.  R_h pairs +x with -x over randomly
+    placed dimensions (so it sums to exactly 0): half the pairs big
+    (2^18 .. 2^20), half fine-grained (1 + m 2^-7).  s_j writes j in two
+    other dimensions as j // 64 and (j % 64) 2^-6, so block-mean scores
+    are j / 64 exactly: distinct, 2^-6 apart, far outside the 1e-4 near-tie
+    window.  A float32 sum of the pooled terms adds the fine values to
+    partial sums near 2^20, whose spacing (2^-3 and up) is coarser than the
+    gap between two candidates' scores."""
+    rng = np.random.default_rng(seed)
+    N = 64 * nb
+    q = torch.ones((1, H, N, D), dtype=torch.bfloat16)
+    kk = np.zeros((1, H, N, D), np.float32)
+    for h in range(H):
+        r = np.zeros(D, np.float64)
+        perm = rng.permutation(D)          # random places for the pairs and the two signal dimensions
+        sig_a, sig_b, pos = perm[0], perm[1], perm[2:]
+        pairs = (D - 2) // 2
+        for p in range(pairs):
+            if p % 2 == 0:
+                x = 2.0 ** rng.integers(18, 21) * (1 + rng.integers(0, 128) / 128.0)
+            else:
+                x = 1 + rng.integers(1, 128) / 128.0
+            x *= 1 if rng.random() < 0.5 else -1
+            r[pos[2 * p]] = x
+            r[pos[2 * p + 1]] = -x
+        for j in range(nb):
+            row = r.copy()
+            row[sig_a] = j // 64
+            row[sig_b] = (j % 64) * 2.0 ** -6
+            kk[0, h, j * 64:(j + 1) * 64, :] = row
+    k = torch.from_numpy(kk).to(torch.bfloat16)
+    assert torch.equal(k.float(), torch.from_numpy(kk)), "construction must be bf16-exact"
+    return q, k
+
+
+@pytest.mark.parametrize("D,nb", [(64, 64), (128, 64), (128, 512)])
+def test_select_cancelling_scores(cuda, D, nb):
+    """Scores reached through large cancelling terms (see cancellation_case):
+    the ranking must follow the exact scores, so masks are bit-exact on every
+    row (none is a near tie), for the selector and the fused call."""
+    H = 8
+    q, k = cancellation_case(D, nb, H, seed=70 + D + nb)
+    budget = 0.5
+    ref, tie = oracle_select(q, k, (), 64, budget)
+    assert tie.sum() == 0
+    bm = run_select(q.to(cuda), k.to(cuda), (), 64, budget)
+    assert compare_masks(bm, ref, tie) == 0
+    if D == 64 and nb <= 64:
+        v = torch.zeros_like(q)
+        _out, bmf = hm.select_forward(q.to(cuda), k.to(cuda), v.to(cuda), hm.Layout(64, []), budget)
+        torch.cuda.synchronize()
+        assert compare_masks(bmf, ref, tie) == 0

@@ -41,7 +41,7 @@ import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
-FP32_PEAK_TFLOPS = 157.3           # MI355X fp32 vector (the fp32 path runs on the VALU)
+FP32_PEAK_TFLOPS = 157.3           # MI355X dense fp32 MFMA (the fp32 path's matrix instruction)
 # the configurations reported under per_config: tiny fp32, SDXL, joint
 # text+image, video (with the radial control), the 64-layer head-masked stack
 PER_CONFIG = ["tiny_fp32", "sdxl_bf16", "joint_text_image_bf16", "video_radial_bf16", "head_masked_stack_bf16"]
@@ -358,7 +358,7 @@ class Run:
         sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
         bf16 = w.dtype == "bf16"
         roof = {"bound": "mfma", "kernel": "attn_mfma_kernel (bsattn_forward)" if bf16
-                else "attn_vec_kernel (bsattn_forward, fp32)",
+                else "attn_f32_kernel (bsattn_forward, fp32 MFMA)",
                 "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": attn_tflops / (MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS),
                 "traffic": profiled_traffic(w.name) if bf16 else None,

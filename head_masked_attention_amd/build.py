@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libbsattn.so")
-SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_vec.hip", "attn_fp8.hip", "stage.cpp"]
+SOURCES = ["bsattn.hip", "select.hip", "attn_mfma.hip", "attn_f32.hip", "attn_fp8.hip", "stage.cpp"]
 HEADERS = ["common.h", "internal.h"]
 # Per-source extra flags.  The attention kernel's scores come out of MFMA
 # accumulators and are never NaN for finite inputs; without NaN semantics

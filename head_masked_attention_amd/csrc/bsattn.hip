@@ -484,7 +484,7 @@ bsattn_status bsattn_forward_masked(const bsattn_tensor* q, const bsattn_tensor*
         e = launch_attn_mfma(a, (int)q->D, s);
     }
     else
-        e = launch_attn_vec(a, q->dtype == BSATTN_F32, (int)q->D, (int)block, s);
+        e = launch_attn_f32(a, q->dtype == BSATTN_F32, (int)q->D, (int)block, s);
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
 

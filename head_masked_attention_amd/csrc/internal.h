@@ -80,7 +80,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int D, const float* q_scale, const
 // bf16 [B][H][N][D] -> e4m3 codes + per-(b, head) scale; amax: B*H words of scratch.
 hipError_t launch_quant_fp8(TView x, TView y, int B, int H, int64_t N, int D, uint32_t* amax, float* scale,
                             hipStream_t s);
-// any supported dtype / block / D: fp32 vector path.
-hipError_t launch_attn_vec(const AttnArgs& a, int dtype_is_f32, int D, int block, hipStream_t s);
+// fp32 inputs, and bf16 of block 32 or D 32: fp32 MFMA path (block 32/64, D 32/64/128).
+hipError_t launch_attn_f32(const AttnArgs& a, int dtype_is_f32, int D, int block, hipStream_t s);
 
 }  // namespace bsattn

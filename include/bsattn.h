@@ -247,10 +247,10 @@ bsattn_status bsattn_radial(const bsattn_layout* layout, double density,
  *        or 64.
  *  head_mask: device uint8 [H], or NULL = every head active.
  *  scale: <= 0 means 1/sqrt(D).
- *  bf16 inputs use the MFMA path (block 64, D 64 or 128; K/V stride_n <= 2^24)
- *  with fp32 softmax
- *  and one final rounding to bf16; fp32 inputs (and other bf16 shapes) use a
- *  fp32 vector path.  Enqueues one kernel; never synchronises.
+ *  bf16 inputs use the bf16 MFMA path (block 64, D 64 or 128; K/V stride_n
+ *  <= 2^24) with fp32 softmax and one final rounding to bf16; fp32 inputs,
+ *  and bf16 of block 32 or D 32, use the fp32 MFMA path (scores, softmax, P
+ *  and accumulation in fp32).  Enqueues one kernel; never synchronises.
  */
 bsattn_status bsattn_forward(const bsattn_tensor* q, const bsattn_tensor* k,
                              const bsattn_tensor* v, const bsattn_block_mask* mask,

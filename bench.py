@@ -98,6 +98,9 @@ def parse():
                    help="skip the per-configuration figures of every workload")
     p.add_argument("--no-reference", action="store_true",
                    help="skip the platform reference figures (torch GEMM and sdpa)")
+    p.add_argument("--kernels-only", choices=["select", "forward", "step", "copy"], default=None,
+                   help="profiling aid: stage the workload, run only this call (or a plain 256 MiB read + "
+                        "256 MiB write copy) --warmup + --steps times, print its time")
     p.add_argument("--graph", action="store_true",
                    help="replay the step (and the per-call loops) as captured HIP graphs instead of "
                         "launching every call from the host")
@@ -465,6 +468,33 @@ def per_config_entry(w, dev, args):
     return e
 
 
+def kernels_only(args, w, dev, stack):
+    """Run one call of the workload (layer 0; every layer for a stacked
+    "step") --warmup + --steps times back to back, for a profiler to see
+    only its kernels.  "copy": a plain elementwise read of 256 MiB and write of
+    256 MiB, the known byte count that scales the HBM fetch/write counters."""
+    if args.kernels_only == "copy":
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: torch.mul(src, 1.0, out=dst)
+    else:
+        r = Run(w, dev, args, stack=stack and args.kernels_only == "step", layer=args.layer)
+        r.select(0, r.stream)      # the block mask the forward reads
+        fn = {"select": lambda: r.select(0, r.stream), "forward": lambda: r.forward(0, r.stream),
+              "step": lambda: r.step(r.stream)}[args.kernels_only]
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": w.name, "call": args.kernels_only, "steps": args.steps,
+                      "ms_per_call": e0.elapsed_time(e1) / max(args.steps, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -475,6 +505,9 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     stack = w.layers > 1 and not args.one_layer
+    if args.kernels_only is not None:
+        kernels_only(args, w, dev, stack)
+        return
     r = Run(w, dev, args, stack=stack, layer=args.layer)
     layers, L = r.layers, len(r.layers)
     fused = r.fused

@@ -232,6 +232,10 @@ __host__ __forceinline__ int64_t attn_grid(int64_t n_work, bool head_masked) {
 // stage tile): lane l's chunk at base + off lands at dst + 16 l.  The loads
 // of a tile share the scalar resource, so each is base plus the lane's
 // 32-bit offset with no per-load address arithmetic.
+// (Kernels build their resources only through helpers like this one: a
+// kernel body that itself named the buffer-resource type compiled without
+// error, but hipcc's host pass then left that file's kernel launch stubs
+// undefined and the library would not load.)
 __device__ __forceinline__ void chunk_to_lds(const void* base, uint32_t off, void* dst) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);

@@ -98,7 +98,7 @@ def parse():
                    help="skip the per-configuration figures of every workload")
     p.add_argument("--no-reference", action="store_true",
                    help="skip the platform reference figures (torch GEMM and sdpa)")
-    p.add_argument("--kernels-only", choices=["select", "forward", "step", "copy"], default=None,
+    p.add_argument("--kernels-only", choices=["select", "forward", "step", "fp8", "copy"], default=None,
                    help="profiling aid: stage the workload, run only this call (or a plain 256 MiB read + "
                         "256 MiB write copy) --warmup + --steps times, print its time")
     p.add_argument("--graph", action="store_true",
@@ -480,8 +480,18 @@ def kernels_only(args, w, dev, stack):
     else:
         r = Run(w, dev, args, stack=stack and args.kernels_only == "step", layer=args.layer)
         r.select(0, r.stream)      # the block mask the forward reads
-        fn = {"select": lambda: r.select(0, r.stream), "forward": lambda: r.forward(0, r.stream),
-              "step": lambda: r.step(r.stream)}[args.kernels_only]
+        if args.kernels_only == "fp8":
+            # the fp8 consumer on the same block mask: Q, K, V quantised once
+            # before the loop, then bsattn_forward_fp8 per call
+            ly0 = r.layers[0]
+            q8, qs = hm.quantize_fp8(ly0["qd"], stream=r.stream)
+            k8, ks = hm.quantize_fp8(ly0["kd"], stream=r.stream)
+            v8, vs = hm.quantize_fp8(ly0["vd"], stream=r.stream)
+            out8 = torch.empty_like(ly0["qd"])
+            fn = lambda: hm.forward_fp8(q8, k8, v8, qs, ks, vs, r.bms[0], ly0["hmd"], out=out8, stream=r.stream)
+        else:
+            fn = {"select": lambda: r.select(0, r.stream), "forward": lambda: r.forward(0, r.stream),
+                  "step": lambda: r.step(r.stream)}[args.kernels_only]
     for _ in range(args.warmup):
         fn()
     torch.cuda.synchronize()

@@ -331,3 +331,34 @@ def test_select_cancelling_scores(cuda, D, nb):
         _out, bmf = hm.select_forward(q.to(cuda), k.to(cuda), v.to(cuda), hm.Layout(64, []), budget)
         torch.cuda.synchronize()
         assert compare_masks(bmf, ref, tie) == 0
+
+
+@pytest.mark.parametrize("D,nb,kind", [(64, 64, "zero_keys"), (128, 64, "equal_blocks"), (64, 256, "zero_keys"),
+                                       (128, 512, "equal_blocks")])
+def test_select_exact_ties_go_to_the_lower_block(cuda, D, nb, kind):
+    """Every non-diagonal score of a row exactly equal (all keys zero, or
+    every key block the same): the pages' rule sends ties to the lower block
+    index, so the kept set is the diagonal plus the lowest k - 1 other
+    candidates.  The oracle flags such rows as near ties, but both sides
+    break exact ties the same way, so here every row is compared."""
+    B, H = 1, 4
+    q, k, _ = workloads.small_case(B=B, H=H, N=64 * nb, D=D, seed=80 + nb)
+    if kind == "zero_keys":
+        k = torch.zeros_like(k)
+    else:
+        k = k[:, :, :64].repeat(1, 1, nb, 1).contiguous()
+    budget = 0.3
+    ref, tie = oracle_select(q, k, (), 64, budget)
+    assert tie.all()
+    bm = run_select(q.to(cuda), k.to(cuda), (), 64, budget)
+    got = download_mask(bm)[0]
+    assert np.array_equal(got, ref)
+    kk = oracle.budget(nb, budget)[0]
+    for i in (0, nb // 2, nb - 1):
+        expect = sorted({i} | set([j for j in range(nb) if j != i][:kk - 1]))
+        assert np.nonzero(ref[0, 0, i])[0].tolist() == expect
+    if D == 64 and nb <= 64:
+        _out, bmf = hm.select_forward(q.to(cuda), k.to(cuda), torch.zeros_like(k).to(cuda), hm.Layout(64, []),
+                                      budget)
+        torch.cuda.synchronize()
+        assert np.array_equal(download_mask(bmf)[0], ref)

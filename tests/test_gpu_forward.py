@@ -276,3 +276,26 @@ def test_forward_steeply_growing_scores(cuda, case, masked):
     got = to64(out)
     assert np.all(np.isfinite(got))
     assert_close(got, ref, "bf16", f"growing scores {name} {'key mask' if masked else 'plain'}")
+
+
+@pytest.mark.parametrize("dtype,D,block", [("bf16", 64, 64), ("bf16", 128, 64), ("fp32", 32, 32)])
+@pytest.mark.parametrize("active", ["none", "one", "last"])
+def test_forward_extreme_head_masks(cuda, dtype, D, block, active):
+    """No active head (every output exactly 0), a single active head, and
+    only the last head active, with a GQA layout: the head-masked work order
+    handles the degenerate counts of active and masked heads."""
+    B, H, Hkv, nb = 2, 8, 2, 6
+    q, k, v = workloads.small_case(B=B, H=H, Hkv=Hkv, N=nb * block, D=D, block=block, dtype=dtype, seed=95)
+    rng = np.random.default_rng(96)
+    mask = (rng.random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+    hmask = np.zeros(H, np.uint8)
+    if active == "one":
+        hmask[3] = 1
+    elif active == "last":
+        hmask[H - 1] = 1
+    out = hm.forward(q.to(cuda), k.to(cuda), v.to(cuda), upload_mask(mask, cuda), torch.from_numpy(hmask).to(cuda))
+    torch.cuda.synchronize()
+    got = to64(out)
+    assert np.all(got[:, hmask == 0] == 0)
+    ref = oracle.attention(to64(q), to64(k), to64(v), block, mask, head_mask=hmask)
+    assert_close(got, ref, dtype, f"head mask {active}")

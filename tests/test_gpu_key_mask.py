@@ -199,3 +199,40 @@ def test_stage_schedule_against_the_oracle(cuda):
     assert d["outcome"] == hm.DECLINE_SHORT
     ones = np.ones((N // 64, N // 64), np.uint8)
     assert_close(to64(out), oracle.attention(q64, k64, v64, 64, ones, key_mask=km), "bf16", "declined short")
+
+
+@pytest.mark.parametrize("dtype,D,block", [("bf16", 64, 64), ("bf16", 128, 64), ("fp32", 64, 32)])
+def test_every_key_masked_gives_zero(cuda, dtype, D, block):
+    """A key mask that masks every key of one batch entry, and for the other
+    only the keys of the last key block: the first entry's rows are all exactly
+    0 (no live key in any kept block), the second entry's rows follow the oracle
+    (rows that keep only the last block are 0 as well).  bf16 and fp32 paths,
+    and the fp8 consumer for the bf16 shapes."""
+    B, H, Hkv, nb = 2, 4, 2, 7
+    N = nb * block
+    q, k, v = workloads.small_case(B=B, H=H, Hkv=Hkv, N=N, D=D, block=block, dtype=dtype, seed=97)
+    rng = np.random.default_rng(98)
+    mask = (rng.random((B, H, nb, nb)) < 0.4).astype(np.uint8)
+    mask[1, 0, 2, :] = 0
+    mask[1, 0, 2, nb - 1] = 1                     # a row keeping only the last block
+    km = np.ones((B, N), np.uint8)
+    km[0, :] = 0
+    km[1, (nb - 1) * block:] = 0
+    kmd = torch.from_numpy(km).to(cuda)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    out = hm.forward(qd, kd, vd, upload_mask(mask, cuda), key_mask=kmd)
+    torch.cuda.synchronize()
+    got = to64(out)
+    assert np.all(got[0] == 0)
+    assert np.all(got[1, 0, 2 * block:3 * block] == 0)
+    ref = oracle.attention(to64(q), to64(k), to64(v), block, mask, key_mask=km)
+    assert_close(got, ref, dtype, "every key masked")
+    if dtype == "bf16":
+        q8, qs = hm.quantize_fp8(qd)
+        k8, ks = hm.quantize_fp8(kd)
+        v8, vs = hm.quantize_fp8(vd)
+        out8 = hm.forward_fp8(q8, k8, v8, qs, ks, vs, upload_mask(mask, cuda), key_mask=kmd)
+        torch.cuda.synchronize()
+        got8 = to64(out8)
+        assert np.all(got8[0] == 0)
+        assert np.all(got8[1, 0, 2 * block:3 * block] == 0)

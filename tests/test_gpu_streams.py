@@ -83,3 +83,53 @@ def test_side_stream_behind_long_work_with_current_stream_churn(lib, cuda):
     ref = oracle.attention(to64(q), to64(k), to64(v), 64, bm.mask.cpu().numpy())
     assert_close(out.float().cpu().numpy(), ref, "bf16", "side-stream forward")
     del junk, a
+
+
+def test_concurrent_host_threads(cuda):
+    """Four host threads, each with its own stream and inputs, call select,
+    forward, select_forward and the fp8 pair at once (ctypes releases the
+    interpreter lock, so the library's entry points run concurrently).  Every
+    result equals the same calls made one after another on one thread."""
+    import threading
+    cases = []
+    for i in range(4):
+        D = 64 if i % 2 == 0 else 128
+        q, k, v = workloads.small_case(B=1, H=4, Hkv=2, N=64 * (10 + 3 * i), D=D, seed=300 + i)
+        cases.append((q.to(cuda), k.to(cuda), v.to(cuda)))
+    lay = hm.Layout(64, [])
+
+    def work(qd, kd, vd, stream):
+        bm = hm.select(qd, kd, lay, 0.3, stream=stream)
+        out = hm.forward(qd, kd, vd, bm, stream=stream)
+        out_f, bm_f = hm.select_forward(qd, kd, vd, lay, 0.3, stream=stream)
+        q8, qs = hm.quantize_fp8(qd, stream=stream)
+        k8, ks = hm.quantize_fp8(kd, stream=stream)
+        v8, vs = hm.quantize_fp8(vd, stream=stream)
+        out8 = hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm, stream=stream)
+        return bm.mask, out, bm_f.mask, out_f, out8
+
+    serial = [work(*c, torch.cuda.current_stream(cuda)) for c in cases]
+    torch.cuda.synchronize()
+    serial = [[t.clone() for t in r] for r in serial]
+    results = [None] * len(cases)
+    errors = []
+    streams = [torch.cuda.Stream(cuda) for _ in cases]
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(3):
+                    results[i] = work(*cases[i], streams[i])
+        except Exception as e:       # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for want, got in zip(serial, results):
+        for a, b in zip(want, got):
+            assert torch.equal(a, b)

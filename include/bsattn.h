@@ -57,7 +57,7 @@ typedef enum {
     BSATTN_ERR_BUDGET = 6,      /* budget/density NaN or <= 0; bad head-mask args      */
     BSATTN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required             */
     BSATTN_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed          */
-    BSATTN_ERR_UNSUPPORTED = 9  /* valid request this build has no kernel for          */
+    BSATTN_ERR_UNSUPPORTED = 9  /* valid request the library has no kernel for         */
 } bsattn_status;
 
 /* Element types of q, k, v and out.  FP8_E4M3 (OCP e4m3: 1 sign, 4 exponent

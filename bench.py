@@ -457,6 +457,12 @@ def per_config_entry(w, dev, args):
                   "calls": "bsattn_select_forward" if r.fused else "bsattn_select + bsattn_forward",
                   "layers_per_step": len(r.layers)},
          "roofline": roof, "selector": sel, "speedup_vs_dense": speed}
+    if not args.no_cold:
+        scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB
+        e["cold"] = {"selector_ms": r.timer.cold(lambda st: r.select(0, st), 11, scratch),
+                     "attention_ms": r.timer.cold(lambda st: r.forward(0, st), 11, scratch),
+                     "note": "median of 11 single calls, each after a 512 MiB scratch write"}
+        del scratch
     if w.radial:
         e["radial"] = r.radial_figures(reps, min(args.warmup, 5))
     hmf = r.head_mask_figures(fwd_ms, reps, min(args.warmup, 5))

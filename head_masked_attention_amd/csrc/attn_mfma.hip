@@ -312,6 +312,21 @@ void attn_mfma_kernel(AttnArgs a) {
     const int gofs = SHARE ? 0 : grp * TILE; // the group's tile within a stage object
     const int hl = lane >> 5, ql = lane & 31;
 
+    // Q^T fragments: lane holds Q[32*wq + ql][16*ks + 8*hl + 0..7].  Without
+    // the fused ranking they are requested before the kept-block count and
+    // list are waited for, so the two memory round trips of a workgroup's
+    // start overlap instead of following each other.
+    const uint16_t* qbase = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qb * BLK * a.q.sn;
+    bf16x8 qf[NKS];
+    auto load_q = [&]() {
+        const uint16_t* qr = qbase + (int64_t)(32 * wq + ql) * a.q.sn + 8 * hl;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
+    };
+    if constexpr (!FUSED) {
+        if (active) load_q();
+    }
+
     int32_t cnt = a.nkb;
     const int32_t* list = nullptr;
     int32_t blk0 = SHARE ? 0 : grp;          // the group's first key block
@@ -341,17 +356,9 @@ void attn_mfma_kernel(AttnArgs a) {
         return;
     }
 
-    const uint16_t* qbase = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qb * BLK * a.q.sn;
     const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.sb + kvh * a.k.sh;
     const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sb + kvh * a.v.sh;
-
-    // Q^T fragments: lane holds Q[32*wq + ql][16*ks + 8*hl + 0..7]
-    bf16x8 qf[NKS];
-    {
-        const uint16_t* qr = qbase + (int64_t)(32 * wq + ql) * a.q.sn + 8 * hl;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
-    }
+    if constexpr (FUSED) load_q();
     // every group runs the same number of stages (the barriers are
     // workgroup-wide); stages past the group's own blocks only synchronise
     const int T = SHARE ? cnt * SUB : ((cnt + SPLIT - 1) / SPLIT) * SUB;

@@ -81,8 +81,8 @@ def profiled_traffic(workload: str):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="sdxl_bf16", choices=sorted(workloads.ALL))
     p.add_argument("--layer", type=int, default=0, help="layer of the stacked workload (with --one-layer)")
     p.add_argument("--one-layer", action="store_true",

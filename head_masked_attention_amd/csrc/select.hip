@@ -349,6 +349,12 @@ struct RankShape {
     static constexpr int RT = 16;                       // rows of the score MFMA tile
     static constexpr int RQ = SPLIT ? 4 : 16;           // rows ranked per workgroup
     static constexpr int WAVES = SPLIT ? 4 : (SHORT ? 16 : 8);
+    // 512 candidates: the LDS holds three workgroups per CU, and the
+    // registers are held to that (six wavefronts per SIMD) with the key-sum
+    // operands loaded per tile instead of one tile ahead -- on the video
+    // shape the 768 workgroups then run in one round (62 -> 55-58 us)
+    static constexpr int MIN_WAVES_PER_SIMD = E == 8 ? 6 : 1;
+    static constexpr bool PREFETCH = MIN_WAVES_PER_SIMD < 6;
 };
 
 // ---------------------------------------------------------------------------
@@ -365,7 +371,8 @@ struct RankShape {
 // index.  Larger candidate sets use 64-bit keys (full score, then position).
 // ---------------------------------------------------------------------------
 template <int D, int E>
-__global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kernel(
+__global__ __launch_bounds__((RankShape<D, E>::WAVES * 64))
+__attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void score_rank_kernel(
     PooledSums qp, PooledSums kp, int B, int H, int Hkv, Geometry g,
     MaskOut out, int n_tiles, int xcd_groups) {
     constexpr int NPAD = 64 * E;
@@ -377,10 +384,16 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
     constexpr int RPW = RQ / WAVES;            // rows per wavefront
     constexpr int RR = RPW >= 2 ? 2 : 1;       // rows ranked together (32-bit keys)
     constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
+    // rows of 256 candidates or more are ranked by radix selection of the
+    // k-th key, shorter ones by a full sort; the counters (2^RADIX_DB of 32
+    // bits) fit in the wavefront's keep rows
+    constexpr bool RADIX = K32 && E >= 4;
+    constexpr int RADIX_DB = RR * NPAD >= 1024 ? 8 : 7;
     constexpr int KQ = D / 4;                  // MFMA k-steps; lane group gq owns d in [gq*KQ, gq*KQ+KQ)
     static_assert(RPW >= 1 && RPW % RR == 0, "rows per wavefront");
+    static_assert(!RADIX || RR * NPAD >= (4 << RADIX_DB), "radix counters fit in the keep rows");
     __shared__ float s_score[RT * SSTR];
-    __shared__ uint8_t s_keep[WAVES][K32 ? RR : 1][NPAD];
+    __shared__ __attribute__((aligned(16))) uint8_t s_keep[WAVES][K32 ? RR : 1][NPAD];
     __shared__ __attribute__((aligned(8))) int16_t s_code[kCodeTable];
     __shared__ int32_t s_rowblk[RT];             // block index of each row of the tile
     const int16_t* codes = fill_codes(g, s_code);
@@ -435,13 +448,18 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
 #pragma unroll
         for (int c = 0; c < KQ / 4; ++c) bv[c] = src[c * 64];
     };
+    constexpr bool PREFETCH = RankShape<D, E>::PREFETCH;
     f4v bnext[KQ / 4];
-    if (wave < n_ct) load_b(wave, bnext);
+    if (PREFETCH && wave < n_ct) load_b(wave, bnext);
     for (int ct = wave; ct < n_ct; ct += WAVES) {
         f4v bv[KQ / 4];
+        if constexpr (PREFETCH) {
 #pragma unroll
-        for (int c = 0; c < KQ / 4; ++c) bv[c] = bnext[c];
-        if (ct + WAVES < n_ct) load_b(ct + WAVES, bnext);
+            for (int c = 0; c < KQ / 4; ++c) bv[c] = bnext[c];
+            if (ct + WAVES < n_ct) load_b(ct + WAVES, bnext);
+        } else {
+            load_b(ct, bv);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT / 16; ++rt) {
             f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -470,10 +488,14 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
     };
 
     // Marks the kept candidates of one row in keep_row (cleared by the
-    // caller) from this wavefront's sorted keys.  pos_of(r): candidate
-    // position of the lane's r-th key (ranks lane * E + r, descending);
-    // score_at(rank): the float32 score at that rank; tb: the keys resolve
-    // scores to 2^-tb relative (0: exact float32 scores).
+    // caller) from this wavefront's ranked keys.  pos_of(r): candidate
+    // position of the lane's r-th key; in_top(r): that key is among the k
+    // largest (the diagonal's included); score_last() and score_next(): the
+    // float32 scores of the k-th and (k + 1)-th largest keys; tb: the keys
+    // resolve scores to 2^-tb relative (0: exact float32 scores).  Slot
+    // lane * E + r holds a candidate exactly when it is below n_cand, both for
+    // keys sorted in descending order (the padding sorts last) and for keys
+    // left in candidate order.
     //
     // Every float32 score is within err = (2 D + 16) 2^-24 |Q_i| max_j |K_j|
     // of the exact block-sum score (the float32 MFMA's accumulation and the
@@ -489,14 +511,15 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
     // diagonal alone) or every candidate is kept.
     __shared__ int16_t s_band[WAVES][64];
     __shared__ double s_bandt[WAVES][64];
-    auto select_row = [&](auto score_at, auto pos_of, int p, int rl, int tb, float qn, uint8_t* keep_row) {
+    auto select_row = [&](auto score_last, auto score_next, auto in_top, auto pos_of, int p, int rl, int tb,
+                          float qn, uint8_t* keep_row) {
         auto mark_sorted = [&]() {
 #pragma unroll
             for (int r = 0; r < E; ++r)
-                if (lane * E + r < g.k) keep_row[pos_of(r)] = 1;
+                if (in_top(r)) keep_row[pos_of(r)] = 1;
         };
         if (g.k < 2 || g.k >= g.n_cand) { mark_sorted(); return; }
-        const float a = score_at(g.k - 1), b = score_at(g.k);
+        const float a = score_last(), b = score_next();
         const float err = (float)(2 * D + 16) * 0x1p-24f * qn * kmax + 0x1p-100f;
         const float T = tb ? ldexpf(fmaxf(fabsf(a), fabsf(b)), 1 - tb) : 0.f;
         const float M = 2.f * err + 2.f * T;
@@ -603,11 +626,37 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
                     key[q][r] = kv;
                 }
             }
-            // the rows' query norms, loaded while the keys sort
+            // the rows' query norms, loaded while the keys are ranked
             float qn[RR];
 #pragma unroll
             for (int q = 0; q < RR; ++q) qn[q] = qnrm[min(p0 + r0 + q, g.n_cand - 1)];
-            wave_bitonic_desc32<RR, E>(key, lane);
+            // the k-th and (k + 1)-th largest key of each row (radix ranking)
+            uint32_t kth[RR], next[RR];
+            if constexpr (RADIX) {
+                // the wavefront's keep rows serve as its radix counters until
+                // they are cleared below
+                uint32_t* hist = (uint32_t*)&s_keep[wave][0][0];
+#pragma unroll
+                for (int q = 0; q < RR; ++q) {
+                    const int p = p0 + r0 + q;
+                    const uint32_t diag = (0xffffffffu << IB) | (IMASK - (uint32_t)p);
+                    kth[q] = 1u;                        // k >= n_cand: every candidate (keys > 0)
+                    next[q] = 0u;
+                    if (r0 + q >= rows || g.k >= g.n_cand) continue;
+                    if (g.k == 1) { kth[q] = diag; continue; }
+                    // the other candidates: neither padding (0) nor the diagonal
+                    bool part[E];
+#pragma unroll
+                    for (int r = 0; r < E; ++r) part[r] = key[q][r] != 0u && key[q][r] < (0xffffffffu << IB);
+                    kth[q] = wave_kth_key<E, RADIX_DB>(key[q], part, g.k - 1, lane, hist);
+                    uint32_t below = 0u;
+#pragma unroll
+                    for (int r = 0; r < E; ++r) below = key[q][r] < kth[q] ? max(below, key[q][r]) : below;
+                    next[q] = __builtin_amdgcn_readfirstlane(wave_max_u32(below));
+                }
+            } else {
+                wave_bitonic_desc32<RR, E>(key, lane);
+            }
 #pragma unroll
             for (int q = 0; q < RR; ++q)
 #pragma unroll
@@ -617,19 +666,29 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
 #pragma unroll
             for (int q = 0; q < RR; ++q) {
                 if (r0 + q >= rows) continue;
-                // the float32 scores at ranks k - 1 (last kept) and k (first
-                // dropped), from the positions in the sorted keys
-                auto score_at = [&](int rank) -> float {
+                // the float32 score of a key (its candidate position in the low bits)
+                auto score_of = [&](uint32_t kv) -> float {
+                    return s_score[(r0 + q) * SSTR + (int)(IMASK - (kv & IMASK))];
+                };
+                // the key at a rank of the sorted keys
+                auto key_at = [&](int rank) -> uint32_t {
                     uint32_t kv = 0u;
 #pragma unroll
                     for (int r = 0; r < E; ++r)
                         if (r == rank % E) kv = key[q][r];
-                    kv = __builtin_amdgcn_readlane(kv, rank / E);
-                    return s_score[(r0 + q) * SSTR + (int)(IMASK - (kv & IMASK))];
+                    return __builtin_amdgcn_readlane(kv, rank / E);
                 };
-                auto pos_of = [&](int r) -> int { return (int)(IMASK - (key[q][r] & IMASK)); };
                 // the kept bits of a 32-bit key resolve scores to 2^-(23 - IB)
-                select_row(score_at, pos_of, p0 + r0 + q, r0 + q, 23 - IB, qn[q], s_keep[wave][q]);
+                if constexpr (RADIX)
+                    select_row([&]() { return score_of(kth[q]); }, [&]() { return score_of(next[q]); },
+                               [&](int r) { return key[q][r] >= kth[q]; },
+                               [&](int r) { return lane * E + r; },
+                               p0 + r0 + q, r0 + q, 23 - IB, qn[q], s_keep[wave][q]);
+                else
+                    select_row([&]() { return score_of(key_at(g.k - 1)); }, [&]() { return score_of(key_at(g.k)); },
+                               [&](int r) { return lane * E + r < g.k; },
+                               [&](int r) { return (int)(IMASK - (key[q][r] & IMASK)); },
+                               p0 + r0 + q, r0 + q, 23 - IB, qn[q], s_keep[wave][q]);
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -666,8 +725,10 @@ __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64)) void score_rank_kern
                 const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)kv, rank / E);
                 return s_score[rl * SSTR + (int)(0xffffffffu - lo32)];
             };
-            auto pos_of = [&](int r) -> int { return (int)(0xffffffffu - (uint32_t)key[r]); };
-            select_row(score_at, pos_of, p, rl, 0, qn, s_keep[wave][0]);
+            select_row([&]() { return score_at(g.k - 1); }, [&]() { return score_at(g.k); },
+                       [&](int r) { return lane * E + r < g.k; },
+                       [&](int r) { return (int)(0xffffffffu - (uint32_t)key[r]); },
+                       p, rl, 0, qn, s_keep[wave][0]);
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
             compact_sparse(p, s_keep[wave][0]);

@@ -362,3 +362,25 @@ def test_select_exact_ties_go_to_the_lower_block(cuda, D, nb, kind):
                                       budget)
         torch.cuda.synchronize()
         assert np.array_equal(download_mask(bmf)[0], ref)
+
+
+@pytest.mark.parametrize("D,nb,budget", [(64, 256, 0.05), (128, 256, 0.3), (64, 512, 0.7), (128, 512, 0.3),
+                                         (32, 512, 0.5)])
+def test_select_scores_over_many_binades(cuda, D, nb, budget):
+    """Key blocks scaled by 2^e (e from -12 to 12) with random signs, a few of
+    them exact copies of another: each row's scores spread over many binades
+    of both signs with exact ties among them, so the rank's ordering of float
+    keys is exercised far from one scale.  Masks bit-exact outside the
+    oracle's near-tie rows (selector paragraph: ranking by score, ties to the
+    lower block)."""
+    B, H = 1, 6
+    q, k, _ = workloads.small_case(B=B, H=H, N=64 * nb, D=D, seed=90 + nb + D)
+    rng = np.random.default_rng(91 + nb + D)
+    scale = np.ldexp(1.0, rng.integers(-12, 13, size=(H, nb))) * rng.choice([-1.0, 1.0], size=(H, nb))
+    kb = k.float().view(B, H, nb, 64, D) * torch.from_numpy(scale).float()[None, :, :, None, None]
+    for dst, src in ((7, 3), (nb // 2, 3), (nb - 1, nb // 3)):
+        kb[:, :, dst] = kb[:, :, src]
+    k = kb.reshape(B, H, 64 * nb, D).to(k.dtype).contiguous()
+    ref, tie = oracle_select(q, k, (), 64, budget)
+    bm = run_select(q.to(cuda), k.to(cuda), (), 64, budget)
+    compare_masks(bm, ref, tie)

@@ -245,16 +245,19 @@ __device__ __forceinline__ void compact_row(const Geometry& g, const int16_t* co
         // the empty asm keeps the four keep() evaluations (LDS reads) ahead
         // of the branches below, so that they are waited for once
         asm volatile("" : "+v"(kbits));
-        uint32_t bits = 0;
-        int c = 0;
+        // bitwise rather than short-circuit logic: selects, not branches
+        uint32_t bits = 0, c = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const bool v = code[u] != -2 && (code[u] == -1 || row_pinned || ((kbits >> u) & 1u));
-            bits |= (uint32_t)v << (8 * u);
-            c += v ? 1 : 0;
+            const uint32_t live = code[u] != -2 ? 1u : 0u;
+            const uint32_t pin = (code[u] == -1 ? 1u : 0u) | (row_pinned ? 1u : 0u);
+            const uint32_t v = live & (pin | ((kbits >> u) & 1u));
+            bits |= v << (8 * u);
+            c += v;
         }
         const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
-        int32_t n = cnt + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
+        // unsigned slot: the store takes the list base from scalar registers
+        uint32_t n = (uint32_t)cnt + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             if ((bits >> (8 * u)) & 1u) irow[n++] = jl + u;
@@ -483,7 +486,7 @@ __attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void s
         compact_row(g, codes, vec4, lane, false, false, out.mask + (slice * nb + i) * nb,
                     out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
                     [&](int32_t j, int32_t code) {
-                        return keep_row[code] != 0 || (w >= 0 && abs(j - i) <= w);
+                        return (keep_row[code] != 0) | ((w >= 0) & (abs(j - i) <= w));
                     });
     };
 

@@ -331,3 +331,26 @@ def test_workspace_bytes(lib):
     assert B_.select_workspace_bytes(2, 10, 10, 4096, 64, 64) == 2 * 2 * 2 * 10 * 64 * 64 * 4 + 2 * 2 * 10 * 64 * 4
     assert B_.select_workspace_bytes(1, 4, 2, 512, 32, 32) == expect(1, 4, 2, 16, 32)
     assert B_.select_workspace_bytes(1, 1, 1, 512, 48, 32) == 0
+
+
+def test_empty_inputs_are_rejected_before_any_launch(lib):
+    """A sequence, batch or head count of zero is a shape error (code 3) at
+    every entry point, returned before anything is enqueued; the outputs are
+    left untouched."""
+    lay, _k = layout()
+    for over in (dict(N=0), dict(B=0), dict(H=0)):
+        q = tensor(**over)
+        out = bmask()
+        assert call_select(lib, q, tensor(), lay, 0.3, out) == 3, over
+        assert call_select(lib, tensor(), q, lay, 0.3, out) == 3, over
+        assert out.k == -7 and out.is_dense == -7
+        assert call_forward(lib, q, tensor(), tensor(), bmask(), tensor()) == 3, over
+        assert call_forward(lib, tensor(), tensor(), tensor(), bmask(), q) == 3, over
+        assert lib.bsattn_select_forward(
+            ctypes.byref(q), ctypes.byref(tensor()), ctypes.byref(tensor()), ctypes.byref(lay), 0.3, None, 0.0,
+            ctypes.byref(tensor()), ctypes.byref(bmask()), FAKE, 1 << 30, None) == 3, over
+    # a mask with no blocks
+    assert call_forward(lib, tensor(), tensor(), tensor(), bmask(nb=0), tensor()) == 3
+    out = bmask(nb=0)
+    assert lib.bsattn_radial(ctypes.byref(lay), 0.3, ctypes.byref(out), None) == 3
+    assert out.k == -7

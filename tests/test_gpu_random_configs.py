@@ -106,3 +106,41 @@ def test_random_config(cuda, c):
         compare_masks(bm_f, ref, tie)
         want_f = oracle.attention(q64, k64, v64, c["block"], download_mask(bm_f)[0], head_mask=c["head_mask"])
         assert_close(to64(out_f), want_f, c["dtype"], case_id(c) + " (select_forward)")
+
+
+def draw_long_case(seed: int) -> dict:
+    """Selections over 129 to 520 blocks (the radix-ranked rows): random
+    layouts with pinned and dropped runs, windows, GQA and budgets from a
+    single kept candidate up to all but one."""
+    rng = np.random.default_rng(5000 + seed)
+    D = int(rng.choice([32, 64, 128]))
+    Hkv = int(rng.integers(1, 3))
+    H = Hkv * int(rng.choice([1, 2]))
+    nb = int(rng.integers(129, 521))
+    N = nb * 64
+    segs = []
+    if rng.random() < 0.7:
+        n_seg = int(rng.integers(2, 6))
+        cuts = np.sort(rng.choice(np.arange(1, N), size=n_seg - 1, replace=False))
+        bounds = [0, *[int(c) for c in cuts], N]
+        segs = [(KINDS[int(rng.integers(len(KINDS)))], bounds[i + 1] - bounds[i]) for i in range(n_seg)]
+        if not any(kd in ("image", "video") for kd, _ in segs):
+            segs[-1] = ("video", segs[-1][1])
+    window = int(rng.choice([0, 0, 96, 640]))
+    mode = rng.random()
+    budget = float(rng.uniform(0.05, 0.95)) if mode < 0.7 else (1e-4 if mode < 0.85 else 0.995)
+    return dict(seed=seed, D=D, H=H, Hkv=Hkv, N=N, segs=segs, window=window, budget=budget)
+
+
+LONG_CASES = [draw_long_case(s) for s in range(24)]
+
+
+@pytest.mark.parametrize("c", LONG_CASES, ids=[f"s{c['seed']}_d{c['D']}_H{c['H']}kv{c['Hkv']}_n{c['N'] // 64}"
+                                                f"_seg{len(c['segs'])}" for c in LONG_CASES])
+def test_random_long_selection(cuda, c):
+    q, k, _ = workloads.small_case(B=1, H=c["H"], Hkv=c["Hkv"], N=c["N"], D=c["D"], seed=7000 + c["seed"])
+    lay = hm.Layout(64, list(c["segs"]), c["window"])
+    bm = hm.select(q.to(cuda), k.to(cuda), lay, c["budget"])
+    torch.cuda.synchronize()
+    ref, tie = oracle.select(to64(q), to64(k), 64, list(c["segs"]), c["budget"], c["window"])
+    compare_masks(bm, ref, tie)

@@ -387,8 +387,8 @@ __attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void s
     constexpr int RPW = RQ / WAVES;            // rows per wavefront
     constexpr int RR = RPW >= 2 ? 2 : 1;       // rows ranked together (32-bit keys)
     constexpr int SSTR = NPAD + 4;             // LDS row stride (floats)
-    // rows of 256 candidates or more are ranked by radix selection of the
-    // k-th key, shorter ones by a full sort; the counters (2^RADIX_DB of 32
+    // rows of more than 128 candidates (padded to 256 or 512) are ranked by
+    // radix selection of the k-th key, shorter ones by a full sort; the counters (2^RADIX_DB of 32
     // bits) fit in the wavefront's keep rows
     constexpr bool RADIX = K32 && E >= 4;
     constexpr int RADIX_DB = RR * NPAD >= 1024 ? 8 : 7;

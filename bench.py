@@ -117,10 +117,17 @@ def kept_flops(count: torch.Tensor, head_mask, block: int, D: int, H: int) -> fl
     return float(c.sum().item()) * 4.0 * block * block * D
 
 
-def selector_bytes(w, bm: hm.BlockMask, n_cand: int) -> float:
-    """Q and K of the sparsifiable tokens read once, mask/count/index written."""
+def selector_bytes(w, bm: hm.BlockMask, n_cand: int, head_mask=None) -> float:
+    """Q and K of the sparsifiable tokens read once, mask/count/index written.
+    Under a head mask (bsattn_select_heads) only the active heads' Q and the
+    K heads they use are read."""
     esize = 2 if w.dtype == "bf16" else 4
-    reads = w.B * (w.H + w.kv_heads) * n_cand * w.block * w.D * esize
+    q_heads, k_heads = w.H, w.kv_heads
+    if head_mask is not None:
+        rep = w.H // w.kv_heads
+        q_heads = int(head_mask.sum())
+        k_heads = int(sum(head_mask[g * rep:(g + 1) * rep].any() for g in range(w.kv_heads)))
+    reads = w.B * (q_heads + k_heads) * n_cand * w.block * w.D * esize
     nb = w.nb
     kept = float(bm.count.to(torch.int64).sum().item())
     writes = w.B * w.H * nb * nb + w.B * w.H * nb * 4 + kept * 4
@@ -289,6 +296,16 @@ class Run:
         hm.select(ly["qd"], ly["kd"], self.layout, self.w.budget if budget is None else budget,
                   out=self.bms[i] if out is None else out, workspace=self.ws, stream=st)
 
+    def select_heads(self, i, st):
+        """The step's selection: under the layer's head mask where it has one
+        (masked heads neither pooled nor ranked), else bsattn_select."""
+        ly = self.layers[i]
+        if ly["hmd"] is None:
+            self.select(i, st)
+            return
+        hm.select_heads(ly["qd"], ly["kd"], self.layout, self.w.budget, ly["hmd"], out=self.bms[i],
+                        workspace=self.ws, stream=st)
+
     def forward(self, i, st, bm=None, head_mask="layer"):
         ly = self.layers[i]
         hmask = ly["hmd"] if isinstance(head_mask, str) else head_mask
@@ -302,7 +319,7 @@ class Run:
 
     def two_call_step(self, st):
         for i in range(len(self.layers)):
-            self.select(i, st)
+            self.select_heads(i, st)
             self.forward(i, st)
 
     def step(self, st):
@@ -374,11 +391,28 @@ class Run:
                "kernels": "pool_kernel + score_rank_kernel (bsattn_select)",
                "note": "avg_call_ms: host-launched calls; graph_call_ms: the same calls replayed from a "
                        "HIP graph (the kernels without the host's launch rate)"}
-        speed = {"attention": dense_ms / fwd_ms, "step": dense_ms / (min(sel_ms, sel_graph_ms) + fwd_ms),
+        step_sel_ms = min(sel_ms, sel_graph_ms)
+        ly0 = self.layers[0]
+        if ly0["hmd"] is not None:
+            # the step's selection under the layer's head mask (bsattn_select_heads)
+            h_ms = t.warm(lambda st: self.select_heads(0, st), reps, warmup)
+            h_graph_ms = h_ms if self.args.graph else Timer(self.dev, self.stream, eager=False).warm(
+                lambda st: self.select_heads(0, st), reps, warmup)
+            torch.cuda.synchronize()
+            h_bytes = selector_bytes(w, self.bms[0], self.n_cand, ly0["hm_np"])
+            self.select(0, self.stream)        # every head's rows again, for the all-heads figure below
+            torch.cuda.synchronize()
+            sel["heads"] = {"avg_call_ms": h_ms, "graph_call_ms": h_graph_ms, "bytes_per_call": h_bytes,
+                            "graph_frac": h_bytes / (h_graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                            "kernels": "pool_kernel + score_rank_kernel (bsattn_select_heads: the masked "
+                                       "heads' Q, and K heads no active head uses, are not pooled; their rows "
+                                       "come back empty)"}
+            step_sel_ms = min(h_ms, h_graph_ms)
+        speed = {"attention": dense_ms / fwd_ms, "step": dense_ms / (step_sel_ms + fwd_ms),
                  "dense_attention_ms": dense_ms, "dense_flops": flops_dense0, "ideal": flops_dense0 / flops0,
                  "note": "attention: the same kernel at budget 1.0 over the 30 % launch; step: that dense "
-                         "launch over selector + attention (the selector's faster of host-launched and "
-                         "graph-replayed time)"}
+                         "launch over the step's selector (bsattn_select_heads under a head mask) + attention "
+                         "(the selector's faster of host-launched and graph-replayed time)"}
         return roof, sel, speed, fwd_ms
 
     def radial_figures(self, reps, warmup):

@@ -62,7 +62,7 @@ EXPORTS = ["bsattn_status_string", "bsattn_layout_classes", "bsattn_budget_k",
            "bsattn_forward_masked", "bsattn_quantize_fp8", "bsattn_forward_fp8", "bsattn_forward_fp8_masked",
            "bsattn_head_mask", "bsattn_mask_density", "bsattn_select_forward",
            "bsattn_stage_create", "bsattn_stage_decide", "bsattn_stage_destroy",
-           "bsattn_stage_outcome_string", "bsattn_select_no_alloc"]
+           "bsattn_stage_outcome_string", "bsattn_select_no_alloc", "bsattn_select_heads"]
 
 class _StageConfig(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("min_length", ctypes.c_int64), ("n_steps", ctypes.c_int32),
@@ -108,6 +108,9 @@ def load_library(path: str = LIB_PATH):
     lib.bsattn_select.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                   ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P,
                                   ctypes.c_size_t, P]
+    lib.bsattn_select_heads.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                        ctypes.POINTER(_Layout), dbl, P, ctypes.POINTER(_BlockMask), P,
+                                        ctypes.c_size_t, P]
     lib.bsattn_radial.argtypes = [ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
     lib.bsattn_select_no_alloc.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
                                            ctypes.POINTER(_Layout), dbl, ctypes.POINTER(_BlockMask), P]
@@ -256,6 +259,39 @@ def select(q, k, layout: Layout, budget: float, *, out: BlockMask | None = None,
                            ctypes.byref(bm), workspace.data_ptr(), workspace.numel(),
                            _stream(q.device, stream))
     _check(st, "bsattn_select")
+    out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
+    return out
+
+
+def select_heads(q, k, layout: Layout, budget: float, head_mask, *, out: BlockMask | None = None,
+                 workspace=None, stream=None) -> BlockMask:
+    """bsattn_select_heads: bsattn_select under a head mask (uint8 device
+    tensor [H], or None for every head); rows of masked heads come back
+    empty and their sums are never pooled."""
+    import torch
+    lib = load_library()
+    B, H, N, D = q.shape
+    nb = N // layout.block
+    hm = None
+    if head_mask is not None:
+        if head_mask.dtype != torch.uint8 or not head_mask.is_cuda:
+            raise BsattnError(2, "bsattn_select_heads", "head_mask must be a uint8 device tensor")
+        if head_mask.numel() != H or not head_mask.is_contiguous():
+            raise BsattnError(3, "bsattn_select_heads", "head_mask must hold one byte per query head")
+        hm = head_mask.data_ptr()
+    need = select_workspace_bytes(B, H, k.shape[1], N, layout.block, D)
+    with _on(stream):
+        if out is None:
+            out = empty_block_mask(B, H, nb, q.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    tq, tk = _tensor(q), _tensor(k)
+    lay, _keep = layout._c()
+    bm = out._c()
+    st = lib.bsattn_select_heads(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(lay), float(budget), hm,
+                                 ctypes.byref(bm), workspace.data_ptr(), workspace.numel(),
+                                 _stream(q.device, stream))
+    _check(st, "bsattn_select_heads")
     out.is_dense, out.k = bool(bm.is_dense), int(bm.k)
     return out
 

@@ -224,13 +224,14 @@ bsattn_status select_validate(const bsattn_tensor* q, const bsattn_tensor* k, co
 
 // The launches of a validated selection; `workspace` holds the pooled sums.
 bsattn_status select_launch(const bsattn_tensor* q, const bsattn_tensor* k, const bsattn_layout* layout,
-                            const Geometry& g, bsattn_block_mask* out, void* workspace, hipStream_t s) {
+                            const Geometry& g, bsattn_block_mask* out, void* workspace, const uint8_t* head_mask,
+                            hipStream_t s) {
     const MaskOut mo{out->mask, out->count, out->index};
     out->k = g.k;
     out->is_dense = g.is_dense;
     hipError_t e;
     if (g.is_dense) {
-        e = launch_layout_fill(g, (int)(q->B * q->H), mo, s);
+        e = launch_layout_fill(g, (int)(q->B * q->H), (int)q->H, head_mask, mo, s);
     } else {
         const PoolSpace ps = pool_space(q->B, q->H, k->H, pooled_rows(g.n_cand), q->D);
         const PooledSums qp = pooled_part(workspace, ps.q_hi, ps.q_lo, ps.q_nrm);
@@ -241,9 +242,10 @@ bsattn_status select_launch(const bsattn_tensor* q, const bsattn_tensor* k, cons
                                      (q->dtype == BSATTN_F32 ? 4 : 2);
         const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
         e = launch_pool(q->dtype == BSATTN_F32, (int)q->D, layout->block, view_of(q), view_of(k),
-                        (int)q->B, (int)q->H, (int)k->H, g, qp, kp, xcd_groups, s);
+                        (int)q->B, (int)q->H, (int)k->H, g, qp, kp, xcd_groups, head_mask, s);
         if (e == hipSuccess)
-            e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, xcd_groups, s);
+            e = launch_score_rank((int)q->D, qp, kp, (int)q->B, (int)q->H, (int)k->H, g, mo, xcd_groups,
+                                  head_mask, s);
     }
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
@@ -251,9 +253,9 @@ bsattn_status select_launch(const bsattn_tensor* q, const bsattn_tensor* k, cons
 
 extern "C" {
 
-bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
-                            const bsattn_layout* layout, double budget, bsattn_block_mask* out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+bsattn_status bsattn_select_heads(const bsattn_tensor* q, const bsattn_tensor* k,
+                                  const bsattn_layout* layout, double budget, const uint8_t* head_mask,
+                                  bsattn_block_mask* out, void* workspace, size_t workspace_bytes, void* stream) {
     Geometry g;
     const bsattn_status st = select_validate(q, k, layout, budget, out, g);
     if (st != BSATTN_OK) return st;
@@ -262,7 +264,13 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
         if (workspace == nullptr) return BSATTN_ERR_WORKSPACE;
         if (workspace_bytes < need || ((uintptr_t)workspace) % 256 != 0) return BSATTN_ERR_WORKSPACE;
     }
-    return select_launch(q, k, layout, g, out, workspace, (hipStream_t)stream);
+    return select_launch(q, k, layout, g, out, workspace, head_mask, (hipStream_t)stream);
+}
+
+bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
+                            const bsattn_layout* layout, double budget, bsattn_block_mask* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return bsattn_select_heads(q, k, layout, budget, nullptr, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -317,7 +325,7 @@ bsattn_status bsattn_select_no_alloc(const bsattn_tensor* q, const bsattn_tensor
         if (need > (size_t)BSATTN_NO_ALLOC_SCRATCH_BYTES) return BSATTN_ERR_WORKSPACE;
         if ((st = scratch_address(&ws)) != BSATTN_OK) return st;
     }
-    return select_launch(q, k, layout, g, out, ws, (hipStream_t)stream);
+    return select_launch(q, k, layout, g, out, ws, nullptr, (hipStream_t)stream);
 }
 
 bsattn_status bsattn_quantize_fp8(const bsattn_tensor* x, bsattn_tensor* out, float* scale, void* ws,
@@ -411,7 +419,7 @@ bsattn_status bsattn_radial(const bsattn_layout* layout, double density, bsattn_
     out->k = g.k;
     out->is_dense = g.is_dense;
     const MaskOut mo{out->mask, out->count, out->index};
-    const hipError_t e = launch_layout_fill(g, out->B * out->H, mo, (hipStream_t)stream);
+    const hipError_t e = launch_layout_fill(g, out->B * out->H, 0, nullptr, mo, (hipStream_t)stream);
     return e == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
 
@@ -541,7 +549,7 @@ bsattn_status bsattn_select_forward(const bsattn_tensor* q, const bsattn_tensor*
     const int64_t pooled_bytes = q->B * k->H * g.n_cand * 64 * q->D * 2;
     const int xcd_groups = pooled_bytes / kNumXcd <= kL2BytesPerXcd ? 1 : 0;
     hipError_t e = launch_pool(0, 64, 64, view_of(q), view_of(k), (int)q->B, (int)q->H, (int)k->H, g,
-                               PooledSums{nullptr, nullptr, nullptr}, kp, xcd_groups, s);
+                               PooledSums{nullptr, nullptr, nullptr}, kp, xcd_groups, nullptr, s);
     if (e != hipSuccess) return BSATTN_ERR_HIP;
     AttnArgs a{};
     a.q = view_of(q);

@@ -61,11 +61,17 @@ __host__ inline PooledSums pooled_part(void* ws, size_t hi, size_t lo, size_t nr
 // lists are written by the XCD whose attention workgroups read them next
 // (chosen by the host when an XCD's share of Q and K fits in its L2).
 // qp.hi NULL: pool K only.
+// head_mask (device uint8 [H] or NULL): the heads whose byte is 0 are not
+// pooled or ranked; their rows are written empty.
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s);
+                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups,
+                       const uint8_t* head_mask, hipStream_t s);
 hipError_t launch_score_rank(int D, PooledSums qp, PooledSums kp, int B, int H, int Hkv,
-                             const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s);
-hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s);
+                             const Geometry& g, MaskOut out, int xcd_groups, const uint8_t* head_mask,
+                             hipStream_t s);
+// slices: B * H (slice b * H + h); the head mask applies when H > 0
+hipError_t launch_layout_fill(const Geometry& g, int slices, int H, const uint8_t* head_mask, MaskOut out,
+                              hipStream_t s);
 // bf16, D 64, block 64, every block a candidate (nkb <= 64), no head or key
 // mask: each workgroup sums its query block, ranks its row against the
 // pooled key sums, writes the row of the block mask and attends over the

@@ -50,7 +50,8 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // norm bound of the hi row, which the score kernel's error bound uses.
 template <typename T, int D, int BLOCK>
 __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int H, int Hkv,
-                                                   Geometry g, PooledSums qp, PooledSums kp, int xcd_groups) {
+                                                   Geometry g, PooledSums qp, PooledSums kp, int xcd_groups,
+                                                   const uint8_t* head_mask) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per token row
     constexpr int RPI = 64 / CPR;              // token rows per wave instruction
@@ -96,6 +97,18 @@ __global__ __launch_bounds__(256) void pool_kernel(TView q, TView k, int B, int 
         p = rem - bh * nc;
         b = bh / heads;
         hh = bh - b * heads;
+    }
+    // under a head mask: a masked query head's Q, and the K of a K/V head
+    // whose query heads are all masked, are never scored
+    if (head_mask != nullptr) {
+        bool live = false;
+        if (is_q) {
+            live = head_mask[hh] != 0;
+        } else {
+            const uint32_t rep = (uint32_t)(H / Hkv);
+            for (uint32_t j = 0; j < rep; ++j) live = live || head_mask[hh * rep + j] != 0;
+        }
+        if (!live) return;
     }
     const T* src_p = (const T*)(is_q ? q.p : k.p);
     const int64_t sb = is_q ? q.sb : k.sb, sh = is_q ? q.sh : k.sh, sn = is_q ? q.sn : k.sn;
@@ -377,7 +390,7 @@ template <int D, int E>
 __global__ __launch_bounds__((RankShape<D, E>::WAVES * 64))
 __attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void score_rank_kernel(
     PooledSums qp, PooledSums kp, int B, int H, int Hkv, Geometry g,
-    MaskOut out, int n_tiles, int xcd_groups) {
+    MaskOut out, int n_tiles, int xcd_groups, const uint8_t* head_mask) {
     constexpr int NPAD = 64 * E;
     constexpr int RT = RankShape<D, E>::RT;
     constexpr int RQ = RankShape<D, E>::RQ;
@@ -417,6 +430,29 @@ __attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void s
     // looked up here, next to the operand loads, rather than at each row's
     // compaction, where every argument read would wait a memory round trip
     if (threadIdx.x < RT) s_rowblk[threadIdx.x] = cand_block(g, p0 + (int)threadIdx.x);
+
+    // a masked head (its sums were never pooled): every row this workgroup
+    // writes is left empty -- mask row 0, count 0
+    if (head_mask != nullptr && head_mask[h] == 0) {
+        const int64_t sl = b * H + h;
+        auto clear_row = [&](int32_t i) {
+            uint8_t* mrow = out.mask + (sl * g.nb + i) * g.nb;
+            for (int32_t j = 4 * lane; j < g.nb; j += 256) {
+                if (vec4) {
+                    *(uint32_t*)(mrow + j) = 0u;
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (j + u < g.nb) mrow[j + u] = 0;
+                }
+            }
+            if (lane == 0) out.count[sl * g.nb + i] = 0;
+        };
+        for (int rl = sub * RQ + wave; rl < sub * RQ + RQ && rl < rows; rl += WAVES) clear_row(cand_block(g, p0 + rl));
+        for (int t = (tile * SPLITS + sub) * WAVES + wave; t < g.n_other; t += n_tiles * SPLITS * WAVES)
+            clear_row(other_block(g, t));
+        return;
+    }
 
     const int64_t prow = pooled_rows(g.n_cand);
     const float* qbase = qp.hi + bh * prow * D;
@@ -754,7 +790,7 @@ __attribute__((amdgpu_waves_per_eu(RankShape<D, E>::MIN_WAVES_PER_SIMD))) void s
 // diagonal by (|i - j|, j) — a contiguous run of candidate positions — plus
 // the window; k = n_cand gives the dense (layout-only) mask.  grid.y = slice.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
+__global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out, int H, const uint8_t* head_mask) {
     __shared__ __attribute__((aligned(8))) int16_t s_code[kCodeTable];
     const int16_t* codes = fill_codes(g, s_code);
     __syncthreads();
@@ -785,7 +821,9 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
         lo = a;
     }
     const int32_t w = g.w;
-    compact_row(g, codes, vec4, lane, code_i == -2, code_i == -1, out.mask + (slice * nb + i) * nb,
+    // every row of a masked head is empty
+    const bool head_off = head_mask != nullptr && head_mask[slice % H] == 0;
+    compact_row(g, codes, vec4, lane, code_i == -2 || head_off, code_i == -1, out.mask + (slice * nb + i) * nb,
                 out.index + (slice * nb + i) * nb, out.count + slice * nb + i,
                 [&](int32_t j, int32_t code) {
                     return (code >= lo && code < lo + kk) || (w >= 0 && abs(j - i) <= w);
@@ -797,59 +835,65 @@ __global__ __launch_bounds__(256) void layout_kernel(Geometry g, MaskOut out) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t launch_pool_t(int block, TView q, TView k, int B, int H, int Hkv,
-                                const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s) {
+                                const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups,
+                                const uint8_t* hmask, hipStream_t s) {
     const int64_t items = (int64_t)B * ((qp.hi == nullptr ? 0 : H) + Hkv) * g.n_cand;
     const int64_t wgs = (items + 3) / 4;
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
-    if (block == 64) return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
-    return launch(pool_kernel<T, D, 32>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups);
+    if (block == 64)
+        return launch(pool_kernel<T, D, 64>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask);
+    return launch(pool_kernel<T, D, 32>, grid, dim3(256), s, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask);
 }
 
 hipError_t launch_pool(int dtype_is_f32, int D, int block, TView q, TView k, int B, int H,
-                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups, hipStream_t s) {
+                       int Hkv, const Geometry& g, PooledSums qp, PooledSums kp, int xcd_groups,
+                       const uint8_t* hmask, hipStream_t s) {
     if (dtype_is_f32) {
-        if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
-        if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
-        return launch_pool_t<float, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+        if (D == 32) return launch_pool_t<float, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
+        if (D == 64) return launch_pool_t<float, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
+        return launch_pool_t<float, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
     }
-    if (D == 32) return launch_pool_t<uint16_t, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
-    if (D == 64) return launch_pool_t<uint16_t, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
-    return launch_pool_t<uint16_t, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, s);
+    if (D == 32) return launch_pool_t<uint16_t, 32>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
+    if (D == 64) return launch_pool_t<uint16_t, 64>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
+    return launch_pool_t<uint16_t, 128>(block, q, k, B, H, Hkv, g, qp, kp, xcd_groups, hmask, s);
 }
 
 template <int D, int E>
 static hipError_t launch_score_t(PooledSums qp, PooledSums kp, int B, int H, int Hkv,
-                                 const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
+                                 const Geometry& g, MaskOut out, int xcd_groups, const uint8_t* hmask,
+                                 hipStream_t s) {
     constexpr int RT = RankShape<D, E>::RT;
     const int n_tiles = (g.n_cand + RT - 1) / RT;
     const int64_t wgs = (int64_t)B * H * n_tiles * (RT / RankShape<D, E>::RQ);
     const dim3 grid((unsigned)(xcd_groups ? (wgs + kNumXcd - 1) / kNumXcd * kNumXcd : wgs));
     return launch(score_rank_kernel<D, E>, grid, dim3(RankShape<D, E>::WAVES * 64), s, qp, kp, B, H, Hkv, g,
-                  out, n_tiles, xcd_groups);
+                  out, n_tiles, xcd_groups, hmask);
 }
 
 template <int D>
 static hipError_t launch_score_d(PooledSums qp, PooledSums kp, int B, int H, int Hkv,
-                                 const Geometry& g, MaskOut out, int xg, hipStream_t s) {
+                                 const Geometry& g, MaskOut out, int xg, const uint8_t* hm, hipStream_t s) {
     const int n = g.n_cand;
-    if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, xg, s);
-    if (n <= 128) return launch_score_t<D, 2>(qp, kp, B, H, Hkv, g, out, xg, s);
-    if (n <= 256) return launch_score_t<D, 4>(qp, kp, B, H, Hkv, g, out, xg, s);
-    if (n <= 512) return launch_score_t<D, 8>(qp, kp, B, H, Hkv, g, out, xg, s);
-    if (n <= 1024) return launch_score_t<D, 16>(qp, kp, B, H, Hkv, g, out, xg, s);
-    return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, xg, s);
+    if (n <= 64) return launch_score_t<D, 1>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
+    if (n <= 128) return launch_score_t<D, 2>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
+    if (n <= 256) return launch_score_t<D, 4>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
+    if (n <= 512) return launch_score_t<D, 8>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
+    if (n <= 1024) return launch_score_t<D, 16>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
+    return launch_score_t<D, 32>(qp, kp, B, H, Hkv, g, out, xg, hm, s);
 }
 
 hipError_t launch_score_rank(int D, PooledSums qp, PooledSums kp, int B, int H, int Hkv,
-                             const Geometry& g, MaskOut out, int xcd_groups, hipStream_t s) {
-    if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
-    if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
-    return launch_score_d<128>(qp, kp, B, H, Hkv, g, out, xcd_groups, s);
+                             const Geometry& g, MaskOut out, int xcd_groups, const uint8_t* hmask,
+                             hipStream_t s) {
+    if (D == 32) return launch_score_d<32>(qp, kp, B, H, Hkv, g, out, xcd_groups, hmask, s);
+    if (D == 64) return launch_score_d<64>(qp, kp, B, H, Hkv, g, out, xcd_groups, hmask, s);
+    return launch_score_d<128>(qp, kp, B, H, Hkv, g, out, xcd_groups, hmask, s);
 }
 
-hipError_t launch_layout_fill(const Geometry& g, int slices, MaskOut out, hipStream_t s) {
+hipError_t launch_layout_fill(const Geometry& g, int slices, int H, const uint8_t* hmask, MaskOut out,
+                              hipStream_t s) {
     const dim3 grid((unsigned)((g.nb + 3) / 4), (unsigned)slices);
-    return launch(layout_kernel, grid, dim3(256), s, g, out);
+    return launch(layout_kernel, grid, dim3(256), s, g, out, H, hmask);
 }
 
 }  // namespace bsattn

@@ -204,6 +204,25 @@ bsattn_status bsattn_select(const bsattn_tensor* q, const bsattn_tensor* k,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * bsattn_select under a per-layer head mask (haagenti_sparse crate docs: the
+ * heads a layer's mask turns off are skipped, their output is zero).
+ *  head_mask: device uint8 [H] (one byte per query head), or NULL for every
+ *  head (then exactly bsattn_select).  The rows of every head with
+ *  head_mask[h] != 0 are bit-identical to bsattn_select's; every row of a
+ *  head with head_mask[h] == 0 is written empty (mask row all 0, count 0,
+ *  index untouched), and that head's Q is not pooled, nor the K of a K/V
+ *  head whose query heads are all masked.  bsattn_forward with the same
+ *  head_mask gives the same output as after bsattn_select.
+ *  Everything else (arguments, workspace, validation, errors, stream) as
+ *  bsattn_select.  The head mask is read on the device, so a mask that
+ *  changes between calls needs no host synchronisation.
+ */
+bsattn_status bsattn_select_heads(const bsattn_tensor* q, const bsattn_tensor* k,
+                                  const bsattn_layout* layout, double budget,
+                                  const uint8_t* head_mask, bsattn_block_mask* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bsattn_select for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments, results, validation and errors as bsattn_select, without

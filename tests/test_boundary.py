@@ -354,3 +354,19 @@ def test_empty_inputs_are_rejected_before_any_launch(lib):
     out = bmask(nb=0)
     assert lib.bsattn_radial(ctypes.byref(lay), 0.3, ctypes.byref(out), None) == 3
     assert out.k == -7
+
+
+def test_select_heads_validation(lib):
+    """bsattn_select_heads validates as bsattn_select does (the head mask is a
+    device pointer read by the kernels; NULL means every head)."""
+    lay, _k = layout()
+    call = lambda q, k, out, budget=0.3, ws=FAKE, ws_bytes=1 << 30, hmask=None: lib.bsattn_select_heads(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(lay), budget, hmask, ctypes.byref(out), ws, ws_bytes, None)
+    for hmask in (None, FAKE):
+        for over, code in ((dict(q=tensor(data=0)), 1), (dict(q=tensor(D=48)), 3), (dict(out=bmask(nb=5)), 3),
+                           (dict(budget=0.0), 6), (dict(ws=0), 7), (dict(q=tensor(N=0)), 3)):
+            args = dict(q=tensor(), k=tensor(), out=bmask(), budget=0.3, ws=FAKE)
+            args.update(over)
+            out = args["out"]
+            assert call(args["q"], args["k"], out, args["budget"], args["ws"], hmask=hmask) == code, (over, hmask)
+            assert out.k == -7 and out.is_dense == -7

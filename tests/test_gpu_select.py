@@ -384,3 +384,64 @@ def test_select_scores_over_many_binades(cuda, D, nb, budget):
     ref, tie = oracle_select(q, k, (), 64, budget)
     bm = run_select(q.to(cuda), k.to(cuda), (), 64, budget)
     compare_masks(bm, ref, tie)
+
+
+HEADS_CASES = [
+    # (name, B, H, Hkv, nb, D, dtype, block, segments, budget, window, head mask)
+    ("sdxl_like", 2, 8, 8, 64, 64, "bf16", 64, (), 0.3, 0, (1, 0, 1, 1, 0, 0, 1, 0)),
+    ("gqa_group_off", 1, 8, 2, 40, 128, "bf16", 64, (), 0.3, 0, (0, 0, 0, 0, 1, 0, 1, 1)),
+    ("layout_window", 1, 4, 4, 50, 128, "bf16", 64,
+     (("conditioning", 64), ("image", 64 * 45), ("padding", 64 * 4)), 0.3, 512, (0, 1, 1, 0)),
+    ("dense_budget", 1, 4, 2, 20, 64, "bf16", 64, (("text", 100), ("image", 64 * 20 - 100)), 1.0, 0, (1, 0, 0, 1)),
+    ("all_masked", 1, 3, 3, 16, 32, "fp32", 32, (), 0.4, 0, (0, 0, 0)),
+    ("none_masked", 1, 3, 1, 16, 64, "bf16", 64, (), 0.4, 0, (1, 1, 1)),
+    ("radix_rows", 1, 4, 4, 300, 64, "bf16", 64, (), 0.3, 0, (1, 0, 0, 1)),
+    ("radix_512", 1, 2, 1, 512, 128, "bf16", 64, (), 0.3, 0, (0, 1)),
+]
+
+
+@pytest.mark.parametrize("case", HEADS_CASES, ids=[c[0] for c in HEADS_CASES])
+def test_select_heads(cuda, case):
+    """bsattn_select_heads: the rows of active heads are bit-identical to
+    bsattn_select's (and so to the oracle outside near ties), every row of a
+    masked head is empty, and attention under the same head mask gives the
+    same output as after bsattn_select (haagenti_sparse crate docs: masked
+    heads are skipped; SD.Next selector paragraph)."""
+    name, B, H, Hkv, nb, D, dtype, block, segs, budget, window, hmask_t = case
+    N = nb * block
+    q, k, v = workloads.small_case(B=B, H=H, Hkv=Hkv, N=N, D=D, block=block, dtype=dtype, seed=120 + nb)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    hmask = np.array(hmask_t, np.uint8)
+    hmd = torch.from_numpy(hmask).to(cuda)
+    lay = hm.Layout(block, list(segs), window)
+    full = hm.select(qd, kd, lay, budget)
+    part = hm.select_heads(qd, kd, lay, budget, hmd)
+    torch.cuda.synchronize()
+    assert part.k == full.k and part.is_dense == full.is_dense
+    mf, cf, idf = download_mask(full)
+    mp, cp, idp = download_mask(part)
+    on = hmask != 0
+    assert np.array_equal(mp[:, on], mf[:, on])
+    assert np.array_equal(cp[:, on], cf[:, on])
+    for b in range(B):
+        for h in np.nonzero(on)[0]:
+            for i in range(nb):
+                assert np.array_equal(idp[b, h, i, :cp[b, h, i]], idf[b, h, i, :cf[b, h, i]])
+    assert not mp[:, ~on].any() and not cp[:, ~on].any()
+    # against the oracle: masked heads' rows empty, the rest as selected
+    ref, tie = oracle_select(q, k, segs, block, budget, window)
+    ref = ref.copy()
+    ref[:, ~on] = 0
+    tie = tie.copy()
+    tie[:, ~on] = 0
+    compare_masks(part, ref, tie)
+    # the forward under the same head mask does not see the difference
+    o_full = hm.forward(qd, kd, vd, full, hmd)
+    o_part = hm.forward(qd, kd, vd, part, hmd)
+    torch.cuda.synchronize()
+    assert torch.equal(o_full, o_part)
+    # no head mask: exactly bsattn_select
+    again = hm.select_heads(qd, kd, lay, budget, None)
+    torch.cuda.synchronize()
+    ma, ca, _ = download_mask(again)
+    assert np.array_equal(ma, mf) and np.array_equal(ca, cf)

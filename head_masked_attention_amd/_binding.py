@@ -570,8 +570,9 @@ def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, ste
     """One attention call through the sparse stage (orchestration only).
 
     Asks the stage whether to serve the call; if it does, runs bsattn_select at
-    the step's budget and bsattn_forward (bsattn_forward_masked when the call
-    carries a token key mask).  A declined self-attention call of a supported
+    the step's budget (bsattn_select_heads under a head mask: the masked heads'
+    rows of the selection come back empty) and bsattn_forward
+    (bsattn_forward_masked when the call carries a token key mask).  A declined self-attention call of a supported
     shape is computed dense by the same kernel (every block kept); a causal
     or cross-attention call returns None for the caller's own attention.
     block_mask: optional caller buffer that receives a served call's
@@ -583,7 +584,7 @@ def sparse_attention(q, k, v, stage: Stage, layout: Layout | None = None, *, ste
                      architecture=architecture, pipeline=pipeline, denoiser=denoiser)
     if d["outcome"] == STAGE_SPARSE:
         lay = layout if layout is not None else Layout(64, [])
-        bm = select(q, k, lay, d["budget"], out=block_mask, stream=stream)
+        bm = select_heads(q, k, lay, d["budget"], head_mask, out=block_mask, stream=stream)
         out = forward(q, k, v, bm, head_mask, out=out, stream=stream,
                       key_mask=key_mask if d["use_key_mask"] else None)
         return out, d

@@ -15,7 +15,7 @@ import torch
 import head_masked_attention_amd as hm
 import oracle
 import workloads
-from parity import assert_close, compare_masks, to64, upload_mask
+from parity import assert_close, compare_masks, download_mask, to64, upload_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -236,3 +236,29 @@ def test_every_key_masked_gives_zero(cuda, dtype, D, block):
         got8 = to64(out8)
         assert np.all(got8[0] == 0)
         assert np.all(got8[1, 0, 2 * block:3 * block] == 0)
+
+
+def test_sparse_attention_under_a_head_mask(cuda):
+    """A served call with a head mask selects only the active heads
+    (bsattn_select_heads): the output equals the forward over a full
+    selection under the same head mask, and the selection's rows of the
+    masked heads are empty."""
+    segs = [("conditioning", 64), ("image", 64 * 20)]
+    N = sum(n for _, n in segs)
+    H = 4
+    q, k, v = workloads.small_case(B=1, H=H, Hkv=2, N=N, D=128, seed=33)
+    qd, kd, vd = q.to(cuda), k.to(cuda), v.to(cuda)
+    hmask = np.array([0, 1, 1, 0], np.uint8)
+    hmd = torch.from_numpy(hmask).to(cuda)
+    lay = hm.Layout(64, segs, 256)
+    stage = hm.Stage(min_length=512, n_steps=4, schedule=0.3)
+    bm = hm.empty_block_mask(1, H, N // 64, cuda)
+    out, d = hm.sparse_attention(qd, kd, vd, stage, lay, step=1, head_mask=hmd, block_mask=bm)
+    torch.cuda.synchronize()
+    assert d["outcome"] == hm.STAGE_SPARSE
+    ref = hm.forward(qd, kd, vd, hm.select(qd, kd, lay, d["budget"]), hmd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    m, c, _ = download_mask(bm)
+    assert not m[:, hmask == 0].any() and not c[:, hmask == 0].any()
+    assert c[:, hmask != 0].all()

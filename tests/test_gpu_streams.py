@@ -87,7 +87,7 @@ def test_side_stream_behind_long_work_with_current_stream_churn(lib, cuda):
 
 def test_concurrent_host_threads(cuda):
     """Four host threads, each with its own stream and inputs, call select,
-    forward, select_forward and the fp8 pair at once (ctypes releases the
+    forward, select_forward, select_heads and the fp8 pair at once (ctypes releases the
     interpreter lock, so the library's entry points run concurrently).  Every
     result equals the same calls made one after another on one thread."""
     import threading
@@ -97,16 +97,18 @@ def test_concurrent_host_threads(cuda):
         q, k, v = workloads.small_case(B=1, H=4, Hkv=2, N=64 * (10 + 3 * i), D=D, seed=300 + i)
         cases.append((q.to(cuda), k.to(cuda), v.to(cuda)))
     lay = hm.Layout(64, [])
+    hmd = torch.tensor([1, 0, 0, 1], dtype=torch.uint8, device=cuda)
 
     def work(qd, kd, vd, stream):
         bm = hm.select(qd, kd, lay, 0.3, stream=stream)
         out = hm.forward(qd, kd, vd, bm, stream=stream)
         out_f, bm_f = hm.select_forward(qd, kd, vd, lay, 0.3, stream=stream)
+        bm_h = hm.select_heads(qd, kd, lay, 0.3, hmd, stream=stream)
         q8, qs = hm.quantize_fp8(qd, stream=stream)
         k8, ks = hm.quantize_fp8(kd, stream=stream)
         v8, vs = hm.quantize_fp8(vd, stream=stream)
         out8 = hm.forward_fp8(q8, k8, v8, qs, ks, vs, bm, stream=stream)
-        return bm.mask, out, bm_f.mask, out_f, out8
+        return bm.mask, out, bm_f.mask, out_f, out8, bm_h.mask, bm_h.count
 
     serial = [work(*c, torch.cuda.current_stream(cuda)) for c in cases]
     torch.cuda.synchronize()

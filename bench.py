@@ -20,6 +20,10 @@ roofline, selector and speedup figures for every configuration (tiny fp32,
 SDXL, joint text+image, video with its radial control, the 64-layer
 head-masked stack with its head-mask skip); `reference` gives the platform's
 own bf16 GEMM and dense sdpa rates on this GPU as context.
+
+Every configuration first runs untimed steps for --prewarm-s seconds (the
+GPU's clocks ramp up over the first tens of ms under load), then --warmup
+untimed steps, then exactly --steps timed steps.
 """
 from __future__ import annotations
 
@@ -83,6 +87,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--prewarm-s", type=float, default=0.5,
+                   help="untimed steps for this many seconds before the warm-up steps of each configuration "
+                        "(the GPU's clocks ramp up under load); 0: none")
     p.add_argument("--workload", default="sdxl_bf16", choices=sorted(workloads.ALL))
     p.add_argument("--layer", type=int, default=0, help="layer of the stacked workload (with --one-layer)")
     p.add_argument("--one-layer", action="store_true",
@@ -330,6 +337,20 @@ class Run:
         for i in range(len(self.layers)):
             self.select_forward(i, st)
 
+    def prewarm(self, seconds: float):
+        """Untimed steps for `seconds` of wall time before any timed region.
+        The GPU's clocks take a few tens of ms of load to reach their steady
+        state (the SDXL step measured 49 us in its first 200 steps and 45 us
+        from about the 500th on, same process), so without this the first
+        figures of a run time the ramp."""
+        if seconds <= 0:
+            return
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                self.step(self.stream)
+            torch.cuda.synchronize()
+
     def time_steps(self, steps: int, warmup: int, fn=None):
         """Host-clocked ms per step over `steps` steps, synchronised on both sides."""
         capture = fn is None and self.args.graph
@@ -480,6 +501,7 @@ def per_config_entry(w, dev, args):
     r = Run(w, dev, args, stack=stack)
     steps = max(2, min(args.steps, 5 if stack else 20))
     warmup = max(1, min(args.warmup, 2 if stack else 5))
+    r.prewarm(args.prewarm_s)
     ms_step = r.time_steps(steps, warmup)
     reps = max(2, min(args.steps, 20))
     roof, sel, speed, fwd_ms = r.kernel_figures(reps, min(args.warmup, 5))
@@ -568,6 +590,7 @@ def main():
     # from the host (--graph captures the step once and replays it).  On
     # MI355X the replayed kernels start with a cold L2, so host launches are
     # the faster default here.
+    r.prewarm(args.prewarm_s)
     ms_per_step = r.time_steps(args.steps, args.warmup)
     two_call_ms = None
     if fused and not args.graph:
@@ -682,6 +705,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": args.prewarm_s,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

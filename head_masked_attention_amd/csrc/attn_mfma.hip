@@ -137,32 +137,56 @@ enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 // K/V stage tile is loaded into LDS once (by all four wavefronts) and read
 // by both heads; there is no merge, each pair writes its own head.
 // FUSED (bsattn_select_forward; D 64, every block of the sequence a candidate,
-// at most 64 of them): wavefront 0 ranks the workgroup's row from its own
-// query block's sum and the selector's pooled key sums, both in float64 --
-// the selector's 32-bit keys and wavefront bitonic sort: the diagonal first,
-// then by score with ties to the lower block, resolved to 2^-17 relative --
-// keeps the top `keep`, writes the row's mask, count and ascending index
-// list, and leaves the list in LDS for the stage loop.
-__device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, int kvh, int qb, int lane,
-                                               int32_t* s_list, uint8_t* s_flag, double* s_qsum) {
+// at most 64 of them): the workgroup ranks its own row from its query block's
+// sum and the selector's pooled key sums, both in float64 -- the selector's
+// 32-bit keys and wavefront bitonic sort: the diagonal first, then by score
+// with ties to the lower block, resolved to 2^-17 relative -- keeps the top
+// `keep`, writes the row's mask, count and ascending index list, and leaves
+// the list in LDS for the stage loop.  The NW wavefronts share the float64
+// work: wavefront w sums query rows [DW w, DW w + DW) (DW = 64 / NW) and
+// scores every candidate over dimensions [DW w, DW w + DW), its query and
+// key-sum loads issued together; the partial sums meet in LDS (`part`: 2 NW
+// x 64 doubles, free until the first stage tiles are requested) in a fixed
+// wavefront order, and wavefront 0 ranks and compacts.  Sums of 64 bf16
+// values are exact in float64 short of extreme exponent spreads, so the
+// query sum is then the pooled one whatever the order.
+template <int NW>
+__device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, int kvh, int qb, int wave, int lane,
+                                               int32_t* s_list, uint8_t* s_flag, double* part) {
     constexpr uint32_t IMASK = 63u;           // 64 candidate positions
+    constexpr int DW = 64 / NW;               // query rows and dimensions per wavefront
+    static_assert(64 % NW == 0 && DW % 8 == 0, "row and dimension shares");
     const int n = a.nkb;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * a.prow * 64;
-    // the query block's sum over its 64 tokens in float64 (token rows
-    // lane / 8 + 8 l of chunk lane % 8, then across the lanes of one chunk);
-    // lanes 0..7 store dimensions 8 lane .. 8 lane + 7 to LDS while the whole
-    // wavefront is active, and every lane reads the sum back from there
+    double* qpart = part;                     // [NW][64] partial query sums
+    double* spart = part + NW * 64;           // [NW][64] partial scores
+    // this wavefront's query rows: lane reads chunk lane % 8 (dimensions
+    // 8 (lane % 8) ..) of rows DW wave + lane / 8 + 8 l
+    uint4 raw[DW / 8];
+    {
+        const uint16_t* qsrc = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh +
+                               ((int64_t)qb * 64 + DW * wave + lane / 8) * a.q.sn + (lane % 8) * 8;
+#pragma unroll
+        for (int l = 0; l < DW / 8; ++l) raw[l] = *(const uint4*)(qsrc + (int64_t)l * 8 * a.q.sn);
+    }
+    // key sums (hi, lo) of candidate `lane` over this wavefront's dimensions;
+    // lanes past the candidates read row 0 (in bounds, unused)
+    float4 kh[DW / 4], kl[DW / 4];
+    {
+        const int cand = lane < n ? lane : 0;
+#pragma unroll
+        for (int m = 0; m < DW / 4; ++m) {
+            const int64_t o = krow0 + pooled_offset<64>(cand, DW * wave + 4 * m);
+            kh[m] = *(const float4*)(a.kp + o);
+            kl[m] = *(const float4*)(a.kp_lo + o);
+        }
+    }
     {
         double qs[8];
-        const uint16_t* qsrc = (const uint16_t*)a.q.p + b * a.q.sb + h * a.q.sh +
-                               ((int64_t)qb * 64 + lane / 8) * a.q.sn + (lane % 8) * 8;
-        uint4 raw[8];
-#pragma unroll
-        for (int l = 0; l < 8; ++l) raw[l] = *(const uint4*)(qsrc + (int64_t)l * 8 * a.q.sn);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qs[e] = 0.0;
 #pragma unroll
-        for (int l = 0; l < 8; ++l) {
+        for (int l = 0; l < DW / 8; ++l) {
             const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -176,31 +200,42 @@ __device__ __forceinline__ void fused_rank_row(const AttnArgs& a, int b, int h, 
             for (int e = 0; e < 8; ++e) qs[e] += lane_xor_f64(qs[e], off);
         if (lane < 8) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_qsum[8 * lane + e] = qs[e];
+            for (int e = 0; e < 8; ++e) qpart[wave * 64 + 8 * lane + e] = qs[e];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // float64 score of the lane's candidate against the selector's key sums
-    // (hi + lo), rounded to float32 for the 32-bit key: the ranking follows
-    // the exact block-mean scores up to 2^-17 relative
+    lds_barrier();                            // every partial query sum in LDS
+    {
+        double sc = 0.0;
+#pragma unroll
+        for (int m = 0; m < DW / 4; ++m) {
+            double qd[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = DW * wave + 4 * m + e;
+                qd[e] = qpart[d];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) qd[e] += qpart[w * 64 + d];
+            }
+            sc = fma(qd[0], (double)kh[m].x + (double)kl[m].x, sc);
+            sc = fma(qd[1], (double)kh[m].y + (double)kl[m].y, sc);
+            sc = fma(qd[2], (double)kh[m].z + (double)kl[m].z, sc);
+            sc = fma(qd[3], (double)kh[m].w + (double)kl[m].w, sc);
+        }
+        spart[wave * 64 + lane] = sc;
+    }
+    lds_barrier();                            // every partial score in LDS
+    if (wave != 0) return;
+    // float64 score of the lane's candidate, rounded to float32 for the
+    // 32-bit key: the ranking follows the exact block-mean scores up to 2^-17
+    // relative
     uint32_t key[1][1] = {{0u}};
     if (lane < n) {
         if (lane == qb) {
             key[0][0] = (0xffffffffu & ~IMASK) | (IMASK - (uint32_t)lane);
         } else {
-            double sc = 0.0;
+            double sc = spart[lane];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int64_t o = krow0 + pooled_offset<64>(lane, 4 * m);
-                const float4 kh = *(const float4*)(a.kp + o);
-                const float4 kl = *(const float4*)(a.kp_lo + o);
-                sc = fma(s_qsum[4 * m + 0], (double)kh.x + (double)kl.x, sc);
-                sc = fma(s_qsum[4 * m + 1], (double)kh.y + (double)kl.y, sc);
-                sc = fma(s_qsum[4 * m + 2], (double)kh.z + (double)kl.z, sc);
-                sc = fma(s_qsum[4 * m + 3], (double)kh.w + (double)kl.w, sc);
-            }
+            for (int w = 1; w < NW; ++w) sc += spart[w * 64 + lane];
             key[0][0] = (orderable((float)sc) & ~IMASK) | (IMASK - (uint32_t)lane);
         }
     }
@@ -340,9 +375,11 @@ void attn_mfma_kernel(AttnArgs a) {
     }
     __shared__ int32_t s_list[FUSED ? 64 : 1];
     __shared__ uint8_t s_flag[FUSED ? 64 : 1];
-    __shared__ __attribute__((aligned(16))) double s_qsum[FUSED ? 64 : 2];
     if constexpr (FUSED) {
-        if (wave == 0) fused_rank_row(a, b, h, kvh, qb, lane, s_list, s_flag, s_qsum);
+        // the ranking's partial sums use the second V stage buffer, whose
+        // first tile is requested only at stage 0's first barrier
+        static_assert(BUF == BUF_K1 && 2 * (2 * SPLIT) * 64 * 8 <= GT * TILE * 2, "ranking partials fit in V1");
+        fused_rank_row<2 * SPLIT>(a, b, h, kvh, qb, wave, lane, s_list, s_flag, (double*)V1);
         lds_barrier();                       // the list in LDS; the mask row's stores drain meanwhile
         cnt = a.keep;
         blk0 = s_list[grp];                  // unused when the group has no block

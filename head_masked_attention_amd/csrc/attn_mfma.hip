@@ -1,10 +1,12 @@
 // Block-sparse attention forward, bf16 MFMA path (gfx950).
 //
 // One workgroup per (b, h, 64-token query block).  A pair of wavefronts
-// covers the 64 query rows (32 each); with SPLIT = 2 a second pair takes every
-// other kept key block and the two partial softmax states are merged at the
-// end.  Each pair walks its share of the compacted list of kept key blocks
-// (CSR-like, ascending) in stages of KT keys:
+// covers the 64 query rows (32 each); with SPLIT = 2 a second pair covers
+// the same rows over the other half of the keys -- at D = 64 the second 32
+// keys of every kept key block, at D = 128 every other kept block -- and the
+// two partial softmax states are merged at the end.
+// Each pair walks the compacted list of kept key blocks (CSR-like, ascending)
+// in stages of KT keys:
 //   - K and V stage tiles go from HBM/L2 straight into LDS with
 //     buffer_load_dwordx4 ... lds (no register staging): V two stages deep, K
 //     one, and the next K tile loads as soon as every wavefront has read
@@ -45,6 +47,12 @@
 // (video length, 24 query heads on 6 K/V heads, radial mask: 4.17 -> 3.91 ms)
 #ifndef BSATTN_GQA_SHARE
 #define BSATTN_GQA_SHARE 1
+#endif
+// 1: with two key-block groups of 32-key stages, group g takes the 32-key
+// half g of every kept block (rather than every other kept block), so both
+// groups run exactly one stage per kept block whatever its count
+#ifndef BSATTN_HALVES
+#define BSATTN_HALVES 1
 #endif
 // 1: a wavefront's issue priority falls as its workgroup progresses
 #ifndef BSATTN_PRIO
@@ -126,10 +134,12 @@ __device__ __forceinline__ void lds_barrier() {
 enum StageBuf { BUF_KV2 = 0, BUF_V1 = 1, BUF_K1 = 2 };
 
 // SPLIT key-block groups per workgroup: group g (wavefronts 2g, 2g + 1)
-// takes the kept blocks at list positions g, g + SPLIT, g + 2 SPLIT, ...
-// with its own LDS stages, and the groups' partial softmax states are merged
-// through LDS at the end.  More wavefronts per query block hide more latency
-// when the grid alone cannot fill the chip.
+// takes keys 32 g .. 32 g + 31 of every kept block at D = 64 (HALVES: both
+// groups run one 32-key stage per kept block), else the kept blocks at list
+// positions g, g + SPLIT, g + 2 SPLIT, ...;
+// each group has its own LDS stages, and the groups' partial softmax states
+// are merged through LDS at the end.  More wavefronts per query block hide
+// more latency when the grid alone cannot fill the chip.
 //
 // SHARE (query heads of a K/V group with one shared block mask): the two
 // wavefront pairs are two query heads of the same K/V head and query block
@@ -364,14 +374,20 @@ void attn_mfma_kernel(AttnArgs a) {
 
     int32_t cnt = a.nkb;
     const int32_t* list = nullptr;
-    int32_t blk0 = SHARE ? 0 : grp;          // the group's first key block
+    // HALVES: the two groups split every kept block (the first half to group
+    // 0, the second to group 1) instead of taking alternate blocks.  At D = 64
+    // (SDXL: 19 kept blocks, 20 stages per group with alternate blocks, 19
+    // with halves) 37.5 against 38.6 us; at D = 128 the halves measured
+    // 0.5-0.8 % slower (joint, video, stack), so there the groups alternate.
+    constexpr bool HALVES = BSATTN_HALVES && !SHARE && SPLIT == 2 && SUB == 2 && D == 64;
+    int32_t blk0 = SHARE || HALVES ? 0 : grp;   // the group's first key block
     if (a.count != nullptr) {
         const int64_t ms = (int64_t)(a.mB == 1 ? 0 : b) * a.mH + (a.mH == 1 ? 0 : h);
         cnt = a.count[ms * a.nqb + qb];
         list = a.index + (ms * a.nqb + qb) * (int64_t)a.nkb;
         // read together with the count rather than after it (an entry of the
         // row either way; unused when the group has no block)
-        blk0 = ((const __attribute__((address_space(4))) int32_t*)list)[!SHARE && grp < a.nkb ? grp : 0];
+        blk0 = ((const __attribute__((address_space(4))) int32_t*)list)[!SHARE && !HALVES && grp < a.nkb ? grp : 0];
     }
     __shared__ int32_t s_list[FUSED ? 64 : 1];
     __shared__ uint8_t s_flag[FUSED ? 64 : 1];
@@ -382,7 +398,7 @@ void attn_mfma_kernel(AttnArgs a) {
         fused_rank_row<2 * SPLIT>(a, b, h, kvh, qb, wave, lane, s_list, s_flag, (double*)V1);
         lds_barrier();                       // the list in LDS; the mask row's stores drain meanwhile
         cnt = a.keep;
-        blk0 = s_list[grp];                  // unused when the group has no block
+        blk0 = s_list[HALVES ? 0 : grp];     // unused when the group has no block
     }
     uint16_t* obase = (uint16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qb * BLK * a.o_sn;
 
@@ -398,17 +414,23 @@ void attn_mfma_kernel(AttnArgs a) {
     if constexpr (FUSED) load_q();
     // every group runs the same number of stages (the barriers are
     // workgroup-wide); stages past the group's own blocks only synchronise
-    const int T = SHARE ? cnt * SUB : ((cnt + SPLIT - 1) / SPLIT) * SUB;
-    const int Tg = SHARE ? T : ((cnt - grp + SPLIT - 1) / SPLIT) * SUB;
+    const int T = SHARE ? cnt * SUB : HALVES ? cnt : ((cnt + SPLIT - 1) / SPLIT) * SUB;
+    const int Tg = SHARE || HALVES ? T : ((cnt - grp + SPLIT - 1) / SPLIT) * SUB;
     // kept key block of stage t: a scalar (constant address space) load, so
     // waiting for it never waits for the stage loads in flight
     const __attribute__((address_space(4))) int32_t* klist =
         (const __attribute__((address_space(4))) int32_t*)list;
     auto block_of = [&](int t) -> int32_t {
+        if constexpr (HALVES) {
+            if constexpr (FUSED) return t == 0 ? blk0 : __builtin_amdgcn_readfirstlane(s_list[t]);
+            return t == 0 ? blk0 : (list == nullptr ? t : klist[t]);
+        }
         const int i = SHARE ? t / SUB : (t / SUB) * SPLIT + grp;
         if constexpr (FUSED) return t < SUB ? blk0 : __builtin_amdgcn_readfirstlane(s_list[i]);
         return t < SUB ? blk0 : (list == nullptr ? i : klist[i]);
     };
+    // first key of stage t within its block
+    auto half_of = [&](int t) -> int { return HALVES ? grp : t % SUB; };
     // per-thread source offsets of the NI chunks it loads per stage: chunk
     // slot s = i*LT + ltid of the tile holds row s / CPR, global chunk
     // (s % CPR) ^ swizzle
@@ -424,7 +446,7 @@ void attn_mfma_kernel(AttnArgs a) {
         voff[i] = (uint32_t)(r * (int32_t)a.v.sn + c * 8) * 2u;
     }
     auto issue_tile = [&](const uint16_t* base, int64_t sn, const uint32_t (&off)[NI], int t, uint16_t* dst) {
-        const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+        const int64_t row0 = (int64_t)block_of(t) * BLK + half_of(t) * KT;
 #pragma unroll
         for (int i = 0; i < NI; ++i) chunk_to_lds(base + row0 * sn, off[i], dst + (i * LT + (SHARE ? wave : wq) * 64) * 8);
     };
@@ -438,7 +460,7 @@ void attn_mfma_kernel(AttnArgs a) {
     uint32_t km_next = 1u;
     auto issue_m = [&](int t) {
         if constexpr (KMASK) {
-            const int64_t row0 = (int64_t)block_of(t) * BLK + (t % SUB) * KT;
+            const int64_t row0 = (int64_t)block_of(t) * BLK + half_of(t) * KT;
             km_next = lane < 32 ? (uint32_t)kmbase[row0 + lane] : 1u;
         }
     };

@@ -262,3 +262,36 @@ def test_sparse_attention_under_a_head_mask(cuda):
     m, c, _ = download_mask(bm)
     assert not m[:, hmask == 0].any() and not c[:, hmask == 0].any()
     assert c[:, hmask != 0].all()
+
+
+@pytest.mark.parametrize("pattern", ["second_half", "first_half", "alternating"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_key_mask_one_half_of_every_block(cuda, pattern, D):
+    # the two wavefront pairs of a workgroup take the two 32-key halves of
+    # every kept block (D 64) or alternate kept blocks (D 128): masking one
+    # half of every block leaves one pair with no live key at all, and rows
+    # with one, two or an odd number of kept blocks split unevenly
+    B, H, nb = 1, 3, 9
+    N = 64 * nb
+    q, k, v = workloads.small_case(B=B, H=H, N=N, D=D, seed=41)
+    rng = np.random.default_rng(42)
+    mask = (rng.random((B, H, nb, nb)) < 0.55).astype(np.uint8)
+    mask[0, 0, 0, :] = 0
+    mask[0, 0, 0, 4] = 1                 # one kept block
+    mask[0, 1, 2, :] = 0
+    mask[0, 1, 2, [1, 7]] = 1            # two
+    mask[0, 2, 5, :] = 1                 # every block (nine)
+    km = np.ones((B, N), np.uint8)
+    for blk in range(nb):
+        lo = 64 * blk
+        if pattern == "second_half" or (pattern == "alternating" and blk % 2 == 0):
+            km[:, lo + 32:lo + 64] = 0
+        else:
+            km[:, lo:lo + 32] = 0
+    out = hm.forward(q.to(cuda), k.to(cuda), v.to(cuda), upload_mask(mask, cuda),
+                     key_mask=torch.from_numpy(km).to(cuda))
+    torch.cuda.synchronize()
+    ref = oracle.attention(to64(q), to64(k), to64(v), 64, mask, key_mask=km)
+    got = to64(out)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", f"{pattern}_d{D}")

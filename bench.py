@@ -433,7 +433,8 @@ class Run:
                  "dense_attention_ms": dense_ms, "dense_flops": flops_dense0, "ideal": flops_dense0 / flops0,
                  "note": "attention: the same kernel at budget 1.0 over the 30 % launch; step: that dense "
                          "launch over the step's selector (bsattn_select_heads under a head mask) + attention "
-                         "(the selector's faster of host-launched and graph-replayed time)"}
+                         "(the selector's faster of host-launched and graph-replayed time); measured_step: that "
+                         "dense launch over the host-timed step per layer (ms_per_step, the calls the step makes)"}
         return roof, sel, speed, fwd_ms
 
     def radial_figures(self, reps, warmup):
@@ -505,6 +506,7 @@ def per_config_entry(w, dev, args):
     ms_step = r.time_steps(steps, warmup)
     reps = max(2, min(args.steps, 20))
     roof, sel, speed, fwd_ms = r.kernel_figures(reps, min(args.warmup, 5))
+    speed["measured_step"] = speed["dense_attention_ms"] * len(r.layers) / ms_step
     flops = sum(r.flops_layers)
     e = {"config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "D": w.D,
                     "block": w.block, "dtype": w.dtype, "budget": w.budget, "k": r.bms[0].k, "layers": w.layers,
@@ -598,6 +600,7 @@ def main():
 
     reps = max(1, min(args.steps, 50))
     roof, sel, speed, fwd_ms = r.kernel_figures(reps, args.warmup)
+    speed["measured_step"] = speed["dense_attention_ms"] * L / ms_per_step
     flops = sum(r.flops_layers)
     flops0 = r.flops_layers[0]
 

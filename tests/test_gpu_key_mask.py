@@ -295,3 +295,22 @@ def test_key_mask_one_half_of_every_block(cuda, pattern, D):
     got = to64(out)
     assert np.isfinite(got).all()
     assert_close(got, ref, "bf16", f"{pattern}_d{D}")
+
+
+def test_key_mask_sdxl_workload_full(cuda):
+    # the bench's key-mask launch: the SDXL workload's 30 % selection with the
+    # last N/16 keys of every batch entry masked, every output row against
+    # the oracle
+    w = workloads.SDXL
+    q, k, v = workloads.make_qkv(w)
+    mask, _tie = oracle.select(to64(q), to64(k), w.block, [], w.budget)
+    km = np.ones((w.B, w.N), np.uint8)
+    km[:, w.N - w.N // 16:] = 0
+    out = hm.forward(q.to(cuda), k.to(cuda), v.to(cuda), upload_mask(mask, cuda),
+                     key_mask=torch.from_numpy(km).to(cuda))
+    torch.cuda.synchronize()
+    ref = oracle.attention(to64(q), to64(k), to64(v), w.block, mask, key_mask=km)
+    got = to64(out)
+    assert np.isfinite(got).all()
+    mx, mean = assert_close(got, ref, "bf16", "sdxl key mask")
+    print(f"[key mask sdxl] max abs {mx:.3g} mean abs {mean:.3g}", flush=True)

@@ -13,6 +13,14 @@ With independent roundings the error of an output is about
 V ~ N(0, 1) that stays below 0.01 typically and below 0.06 in the worst of
 ~10^6 outputs, plus bf16 output rounding (2^-9 relative).  Bar: max abs
 6e-2, mean abs 6e-3.
+
+Rows whose weight sits on a few keys move by the rounding of those weights
+themselves: with two keys of weights w and 1 - w, the output moves by
+w (1 - w) |d1 - d2| |v1 - v2| <= 2^-5 |v1 - v2|.  The clustered SDXL
+workload's rows are of that kind; rounding P to E4M3 alone (exact row
+maximum, round to nearest even, computed on the CPU over its 5.2 million
+outputs) moves them by up to 0.135 (mean 0.0042).  Bar for that workload:
+max abs 0.15, mean abs 6e-3.
 """
 import numpy as np
 import pytest
@@ -27,6 +35,7 @@ pytestmark = pytest.mark.gpu
 
 FP8_MAX_ABS = 6e-2
 FP8_MEAN_ABS = 6e-3
+FP8_PEAKED_MAX_ABS = 0.15     # the clustered SDXL workload (rows concentrated on few keys)
 
 
 @pytest.mark.parametrize("B,H,N,D", [(2, 3, 64 * 5, 128), (1, 4, 64 * 7, 64), (1, 2, 32 * 9, 32)])
@@ -54,11 +63,11 @@ def run_fp8(cuda, q, k, v, mask=None, hmask=None):
     return to64(out), deq
 
 
-def check(got, ref, what):
+def check(got, ref, what, max_abs=FP8_MAX_ABS):
     err = np.abs(got - ref)
     print(f"[fp8 {what}] max abs {err.max():.3g} mean abs {err.mean():.3g}", flush=True)
     assert np.isfinite(got).all()
-    assert err.max() <= FP8_MAX_ABS, what
+    assert err.max() <= max_abs, what
     assert err.mean() <= FP8_MEAN_ABS, what
 
 
@@ -102,7 +111,18 @@ def test_forward_fp8_dense_sdxl_shape(cuda):
                      np.random.default_rng(75).integers(0, w.N, 256)], 1)
     ref = oracle.attention(*deq, 64, bm.mask.cpu().numpy(), rows=rows)
     got = to64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    check(got, ref, "sdxl sampled rows")
+    check(got, ref, "sdxl sampled rows", max_abs=FP8_PEAKED_MAX_ABS)
+
+
+def test_forward_fp8_sdxl_workload_full(cuda):
+    # the bench's fp8 launch: the whole SDXL workload (both batch entries,
+    # every head) over the oracle's 30 % selection, every output row
+    w = workloads.SDXL
+    q, k, v = workloads.make_qkv(w)
+    mask, _tie = oracle.select(to64(q), to64(k), w.block, [], w.budget)
+    got, (qd, kd, vd) = run_fp8(cuda, q, k, v, mask)
+    ref = oracle.attention(qd, kd, vd, 64, mask)
+    check(got, ref, "sdxl workload", max_abs=FP8_PEAKED_MAX_ABS)
 
 
 def key_mask_fp8(B, N, seed):

@@ -29,7 +29,7 @@ import torch
 import head_masked_attention_amd as hm
 import oracle
 import workloads
-from parity import to64, upload_mask
+from parity import sample_rows, to64, upload_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,26 @@ def test_forward_fp8_sdxl_workload_full(cuda):
     got, (qd, kd, vd) = run_fp8(cuda, q, k, v, mask)
     ref = oracle.attention(qd, kd, vd, 64, mask)
     check(got, ref, "sdxl workload", max_abs=FP8_PEAKED_MAX_ABS)
+
+
+@pytest.mark.parametrize("name,max_abs", [("joint_text_image_bf16", FP8_PEAKED_MAX_ABS),
+                                          ("video_radial_bf16", FP8_MAX_ABS)])
+def test_forward_fp8_large_workload_sampled(cuda, name, max_abs):
+    # the fp8 launch at the joint text+image (clustered Q/K: peaked rows) and
+    # video (iid) sizes over the oracle's selection, on sampled rows of every
+    # block class (pinned text rows, sparse rows at both ends, padding rows)
+    from test_gpu_forward import _layout_blocks
+    w = workloads.ALL[name]
+    q, k, v = workloads.make_qkv(w)
+    mask, _tie = oracle.select(to64(q), to64(k), w.block, list(w.segments), w.budget)
+    got, (qd, kd, vd) = run_fp8(cuda, q, k, v, mask)
+    cls = oracle.classes(list(w.segments), w.N, w.block)
+    rows = sample_rows(w.B, w.H, w.nb, w.block, _layout_blocks(w, cls), 6, seed=76)
+    ref = oracle.attention(qd, kd, vd, w.block, mask, rows=rows)
+    check(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, f"{name} sampled rows", max_abs=max_abs)
+    dropped = np.nonzero(cls == oracle.DROPPED)[0]
+    for qb in dropped:
+        assert np.all(got[:, :, qb * w.block:(qb + 1) * w.block] == 0)
 
 
 def key_mask_fp8(B, N, seed):

@@ -16,11 +16,11 @@ V ~ N(0, 1) that stays below 0.01 typically and below 0.06 in the worst of
 
 Rows whose weight sits on a few keys move by the rounding of those weights
 themselves: with two keys of weights w and 1 - w, the output moves by
-w (1 - w) |d1 - d2| |v1 - v2| <= 2^-5 |v1 - v2|.  The clustered SDXL
-workload's rows are of that kind; rounding P to E4M3 alone (exact row
-maximum, round to nearest even, computed on the CPU over its 5.2 million
-outputs) moves them by up to 0.135 (mean 0.0042).  Bar for that workload:
-max abs 0.15, mean abs 6e-3.
+w (1 - w) |d1 - d2| |v1 - v2| <= 2^-5 |v1 - v2|.  The clustered workloads'
+rows (SDXL, joint text+image) are of that kind; rounding P to E4M3 alone
+(exact row maximum, round to nearest even, computed on the CPU over the SDXL
+workload's 5.2 million outputs) moves them by up to 0.135 (mean 0.0042).
+Bar for those workloads: max abs 0.15, mean abs 6e-3.
 """
 import numpy as np
 import pytest
